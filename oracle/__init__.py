@@ -1,0 +1,304 @@
+"""ORACLE -- test infrastructure only.
+
+A plain, slow CPU statement of what the sink + window KV-cache chunk attention
+computes.  Only the tests, the smoke check and the CPU-baseline leg of the
+benchmark import it; the product library never does, and this package imports
+nothing from the product package.  It shares no code with the GPU path.
+
+Sources (cited by page title and section):
+
+* "LingBot-World-Infinity: The Open-Source World Model That Refuses to Forget"
+  (repo-explainer page), sections "The trick: treat video like a causal
+  stream" (the simplified loop: keep the anchor tokens, evict old tokens, step,
+  append) and "How the cache keeps the world alive" (a sliding KV cache with
+  sink tokens kept at the front, old tokens discarded once the window is full).
+* "Westlake AGI Lab's 'World in World' Steers Frozen Video Models", second
+  paragraph: the native block holds 18 latent-frame slots -- six anchors, eight
+  recent finalized states and four states of the current chunk.
+* "Infinite Worlds with Versatile Interactions", paragraph on causal
+  pretraining: each frame state depends only on past observations; the
+  teacher-forcing mask; MoBA appends a fully bidirectional block to it; a
+  causal cross-attention mask keeps chunk-wise prompts from leaking future
+  semantics.
+* "Mix Forcing: Causal Pre-Training via Mixture Attention for Interactive
+  World Models", Overview, "Mix the training modes" and "Condition each chunk":
+  chunks are generated from current inputs and cached history; MoBA mixes
+  teacher forcing with bidirectional training; each chunk's cross-attention
+  reads the shared environment prompt and its own local prompt only.
+
+Readings where the pages are silent (all stated once more in the design notes):
+sinks and window are counted in latent frames; the window excludes the current
+chunk; append and evict happen in one call after a chunk is finalized; an
+append longer than the window keeps only its last W non-sink frames; the
+current chunk attends itself bidirectionally; MoBA clean chunks are
+block-causal among themselves; the MoBA bidirectional block attends only
+itself and nothing else attends it; a row with no allowed key outputs zero.
+
+Numerics: the attention arithmetic is in ``attend.c`` (fp64, two-pass
+softmax).  Integer parts (slot arithmetic, resident sets, masks as key
+intervals) are here, in Python.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+# --------------------------------------------------------------------------------------------
+# Build / load of the fp64 attention core
+# --------------------------------------------------------------------------------------------
+
+def build(verbose=False):
+    """Compile ``liboracle.so`` from ``attend.c`` with gcc (OpenMP, no BLAS)."""
+    cmd = ["gcc", "-O3", "-march=x86-64-v3", "-fopenmp", "-fPIC", "-shared",
+           os.path.join(_DIR, "attend.c"), "-o", os.path.join(_DIR, "liboracle.so"), "-lm"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"oracle build failed:\n{r.stdout}\n{r.stderr}")
+    if verbose and r.stderr:
+        print(r.stderr)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = os.path.join(_DIR, "liboracle.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        lib.oracle_attend.restype = ctypes.c_int
+        lib.oracle_attend.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+        _lib = lib
+    return _lib
+
+
+def widen(x):
+    """float32 view of an input: bf16 bit patterns (uint16) are widened exactly, float32 passes."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if x.dtype == np.float32:
+        return x
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+def attend(q, k, v, intervals, scale, want_probs=False):
+    """Masked softmax attention in fp64 (``attend.c``).
+
+    q: [nq][H][D]; k, v: [nk][H][D] (float32 or bf16 bits as uint16).
+    intervals: list (one entry per query row) of lists of disjoint half-open
+    key ranges (lo, hi) into k/v.  Returns out [nq][H][D] float64, and the
+    dense probabilities [nq][H][nk] when ``want_probs``.
+    """
+    q = np.ascontiguousarray(widen(q))
+    k = np.ascontiguousarray(widen(k))
+    v = np.ascontiguousarray(widen(v))
+    nq, H, D = q.shape
+    nk = k.shape[0]
+    if k.shape != (nk, H, D) or v.shape != (nk, H, D):
+        raise ValueError("k/v shape mismatch")
+    if len(intervals) != nq:
+        raise ValueError("one interval list per query row is required")
+    ptr = np.zeros(nq + 1, dtype=np.int64)
+    los, his = [], []
+    for i, ivs in enumerate(intervals):
+        ivs = sorted((int(a), int(b)) for a, b in ivs if b > a)
+        for (a0, b0), (a1, _) in zip(ivs, ivs[1:]):
+            if a1 < b0:
+                raise ValueError(f"row {i}: overlapping key intervals")
+        for a, b in ivs:
+            los.append(a)
+            his.append(b)
+        ptr[i + 1] = ptr[i] + len(ivs)
+    lo = np.asarray(los, dtype=np.int64) if los else np.zeros(1, dtype=np.int64)
+    hi = np.asarray(his, dtype=np.int64) if his else np.zeros(1, dtype=np.int64)
+    out = np.empty((nq, H, D), dtype=np.float64)
+    probs = np.empty((nq, H, nk), dtype=np.float64) if want_probs else None
+    rc = _load().oracle_attend(q.ctypes.data, nq, k.ctypes.data, v.ctypes.data, nk, H, D, ptr.ctypes.data,
+                               lo.ctypes.data, hi.ctypes.data, float(scale), out.ctypes.data,
+                               probs.ctypes.data if probs is not None else None)
+    if rc != 0:
+        raise RuntimeError(f"oracle_attend failed ({rc})")
+    return (out, probs) if want_probs else out
+
+
+# --------------------------------------------------------------------------------------------
+# Cache policy: sinks + sliding window, counted in latent frames
+# ("How the cache keeps the world alive"; 18-slot layout of "World in World")
+# --------------------------------------------------------------------------------------------
+
+def slot_of_frame(f, S, W):
+    """Slot of frame f: the first S frames own slots 0..S-1 for good; later frames
+    share the W window slots in turn, so frame f overwrites frame f-W."""
+    return f if f < S else S + (f - S) % W
+
+
+def resident_frames(F, S, W):
+    """Frames held after F frames were appended, in time order: the sinks
+    (the first min(F, S) frames) and the last W non-sink frames."""
+    return list(range(min(F, S))) + list(range(max(S, F - W), F))
+
+
+def valid_slots(F, S, W):
+    """Number of filled slots after F appended frames."""
+    return min(F, S) + min(max(F - S, 0), W)
+
+
+def frames_kept_by_append(F, n, S, W):
+    """Frames of an append of n frames (frames F..F+n-1) that are still resident
+    after it: sinks, and the last W non-sink frames.  The others would be
+    evicted by the same call and are never written."""
+    return [f for f in range(F, F + n) if f < S or f >= F + n - W]
+
+
+class CacheModel:
+    """One layer of the KV cache, kept as a map frame -> its K/V rows.
+
+    ``append`` follows the loop of the repo-explainer page (evict old non-sink
+    frames, keep the anchors, append the finalized frames); here the eviction
+    and the append are one call made after a chunk is finalized.
+    """
+
+    def __init__(self, S, W, tokens_per_frame, H, D, dtype=np.uint16):
+        if S < 0 or W < 1 or tokens_per_frame < 1:
+            raise ValueError("need S >= 0, W >= 1, tokens_per_frame >= 1")
+        self.S, self.W, self.tpf, self.H, self.D, self.dtype = S, W, tokens_per_frame, H, D, dtype
+        self.F = 0
+        self.frames = {}  # frame index -> (k rows [tpf][H][D], v rows [tpf][H][D])
+
+    def append(self, k_new, v_new, n_frames):
+        k_new = np.asarray(k_new).reshape(n_frames * self.tpf, self.H, self.D)
+        v_new = np.asarray(v_new).reshape(n_frames * self.tpf, self.H, self.D)
+        for f in frames_kept_by_append(self.F, n_frames, self.S, self.W):
+            j = f - self.F
+            rows = slice(j * self.tpf, (j + 1) * self.tpf)
+            self.frames[f] = (k_new[rows].copy(), v_new[rows].copy())
+        self.F += n_frames
+        keep = set(resident_frames(self.F, self.S, self.W))
+        self.frames = {f: kv for f, kv in self.frames.items() if f in keep}
+
+    def resident(self):
+        return resident_frames(self.F, self.S, self.W)
+
+    def slot_map(self):
+        """frame held by each of the S+W slots, -1 where empty."""
+        m = np.full(self.S + self.W, -1, dtype=np.int64)
+        for f in self.resident():
+            m[slot_of_frame(f, self.S, self.W)] = f
+        return m
+
+    def slot_buffers(self):
+        """K and V laid out by slot, [S+W][tpf][H][D]; empty slots are zero."""
+        shape = (self.S + self.W, self.tpf, self.H, self.D)
+        kb = np.zeros(shape, dtype=self.dtype)
+        vb = np.zeros(shape, dtype=self.dtype)
+        for f in self.resident():
+            s = slot_of_frame(f, self.S, self.W)
+            kb[s], vb[s] = self.frames[f]
+        return kb, vb
+
+    def logical_kv(self):
+        """Resident K and V concatenated in time order, [n_resident*tpf][H][D]."""
+        fs = self.resident()
+        if not fs:
+            e = np.zeros((0, self.H, self.D), dtype=self.dtype)
+            return e, e.copy()
+        return (np.concatenate([self.frames[f][0] for f in fs]),
+                np.concatenate([self.frames[f][1] for f in fs]))
+
+
+# --------------------------------------------------------------------------------------------
+# Chunk attention at inference ("Mix Forcing" Overview: chunks from current inputs and
+# cached history; "World in World": anchors + recent + current chunk slots)
+# --------------------------------------------------------------------------------------------
+
+def chunk_attention(cache, q, segments, scale, rows=None):
+    """Queries of the current chunk attend every resident cache frame and every
+    token of the passed segments (the current chunk's own K/V, bidirectionally,
+    or prompt K/V for cross-attention).  ``cache`` may be None.
+
+    q: [nq][H][D]; segments: list of (k, v), each [n][H][D].  ``rows`` selects
+    the query rows to evaluate (default: all).  Returns fp64 [len(rows)][H][D].
+    """
+    ks, vs = [], []
+    if cache is not None:
+        kc, vc = cache.logical_kv()
+        ks.append(kc)
+        vs.append(vc)
+    for k, v in segments:
+        ks.append(np.asarray(k))
+        vs.append(np.asarray(v))
+    k_all = np.concatenate([widen(x) for x in ks]) if ks else np.zeros((0,) + q.shape[1:], np.float32)
+    v_all = np.concatenate([widen(x) for x in vs]) if vs else np.zeros((0,) + q.shape[1:], np.float32)
+    q = np.asarray(q)
+    if rows is not None:
+        q = q[np.asarray(rows)]
+    nk = k_all.shape[0]
+    return attend(q, k_all, v_all, [[(0, nk)]] * q.shape[0], scale)
+
+
+# --------------------------------------------------------------------------------------------
+# MoBA training mask ("Infinite Worlds with Versatile Interactions", causal pretraining
+# paragraph; "Mix Forcing", "Mix the training modes")
+# --------------------------------------------------------------------------------------------
+
+def moba_row_intervals(i, tokens_per_frame, frames, chunk_frames, bidir_block=1):
+    """Allowed key ranges of token i in the sequence [clean | noisy | bidirectional].
+
+    Each part holds ``frames`` latent frames; a token's frame g inside its part
+    lies in chunk k = g // chunk_frames.  Clean tokens see clean keys of chunks
+    <= k (block-causal); noisy tokens see clean keys of chunks < k and noisy
+    keys of chunk k (teacher forcing); tokens of the bidirectional block see
+    the whole block and nothing else.
+    """
+    L = frames * tokens_per_frame
+    cl = chunk_frames * tokens_per_frame
+    part, r = divmod(i, L)
+    k = (r // tokens_per_frame) // chunk_frames
+    if part == 0:
+        return [(0, min((k + 1) * cl, L))]
+    if part == 1:
+        out = [(0, min(k * cl, L))] if k > 0 else []
+        out.append((L + k * cl, L + min((k + 1) * cl, L)))
+        return out
+    if part == 2 and bidir_block:
+        return [(2 * L, 3 * L)]
+    raise ValueError("token index outside the sequence")
+
+
+def moba_attention(q, k, v, tokens_per_frame, frames, chunk_frames, bidir_block, scale, rows=None):
+    """MoBA-masked attention over the whole training sequence; fp64 rows."""
+    q = np.asarray(q)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    ivs = [moba_row_intervals(int(i), tokens_per_frame, frames, chunk_frames, bidir_block) for i in rows]
+    return attend(q[rows], k, v, ivs, scale)
+
+
+# --------------------------------------------------------------------------------------------
+# Chunk-wise causal cross-attention ("Mix Forcing", "Condition each chunk")
+# --------------------------------------------------------------------------------------------
+
+def cross_row_intervals(chunk, env_tokens, local_tokens):
+    """Over keys [env | local_0 | local_1 | ...]: chunk i reads env and local_i only."""
+    a = env_tokens + chunk * local_tokens
+    return [(0, env_tokens), (a, a + local_tokens)]
+
+
+def cross_attention(q, chunk, k_env, v_env, k_locals, v_locals, scale, rows=None):
+    """Queries of chunk ``chunk`` attend the environment prompt and their own local prompt."""
+    k_all = np.concatenate([widen(k_env)] + [widen(x) for x in k_locals])
+    v_all = np.concatenate([widen(v_env)] + [widen(x) for x in v_locals])
+    q = np.asarray(q)
+    if rows is not None:
+        q = q[np.asarray(rows)]
+    iv = cross_row_intervals(chunk, k_env.shape[0], k_locals[0].shape[0])
+    return attend(q, k_all, v_all, [iv] * q.shape[0], scale)

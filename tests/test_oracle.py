@@ -1,0 +1,494 @@
+"""Pins of the oracle: brute force, invariants, closed forms, layout and traces.
+
+Every check here compares the oracle with something other than itself: a
+dense NumPy fp64 masked softmax built from a per-pair mask predicate, a list
+simulation of the pages' generation loop, a mathematical identity, or a count
+derived by hand from the pages (fixtures under tests/golden/).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built():
+    if not os.path.exists(os.path.join(os.path.dirname(oracle.__file__), "liboracle.so")):
+        oracle.build()
+    if not os.path.exists(os.path.join(os.path.dirname(synth.__file__), "libsynth_cpu.so")):
+        synth.build()
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+
+
+def dense_masked_softmax(q, k, v, mask, scale):
+    """Brute force: scores for every pair, -inf where masked, softmax, times V (fp64)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    s = np.einsum("ihd,jhd->hij", q, k) * scale            # [H][nq][nk]
+    s = np.where(mask[None, :, :], s, -np.inf)
+    m = np.max(s, axis=-1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    p = np.exp(s - m)
+    den = p.sum(-1, keepdims=True)
+    p = np.divide(p, den, out=np.zeros_like(p), where=den > 0)
+    return np.einsum("hij,jhd->ihd", p, v), p
+
+
+def mask_from_intervals(ivs, nk):
+    m = np.zeros((len(ivs), nk), dtype=bool)
+    for i, row in enumerate(ivs):
+        for a, b in row:
+            m[i, a:b] = True
+    return m
+
+
+# ---------------------------------------------------------------------------------------------
+# attention core vs brute force
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nq,nk,H,D", [(5, 11, 3, 7), (17, 40, 2, 64), (1, 1, 1, 1), (9, 33, 4, 128)])
+def test_attend_matches_dense_brute_force(nq, nk, H, D):
+    rng = np.random.default_rng(nq * 1000 + nk)
+    q, k, v = _rand((nq, H, D), 1), _rand((nk, H, D), 2), _rand((nk, H, D), 3)
+    ivs = []
+    for i in range(nq):
+        cuts = np.sort(rng.choice(nk + 1, size=4, replace=True))
+        ivs.append([(int(cuts[0]), int(cuts[1])), (int(cuts[2]), int(cuts[3]))])
+    ivs[0] = [(0, nk)]
+    scale = 0.37
+    out, probs = oracle.attend(q, k, v, ivs, scale, want_probs=True)
+    ref, pref = dense_masked_softmax(q, k, v, mask_from_intervals(ivs, nk), scale)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(probs, pref.transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+def test_probabilities_sum_to_one():
+    """I1: every softmax row with at least one allowed key sums to one."""
+    q, k, v = _rand((12, 2, 16), 4), _rand((30, 2, 16), 5), _rand((30, 2, 16), 6)
+    ivs = [[(0, 3 + i)] if i % 3 else [(2, 9), (20, 30)] for i in range(12)]
+    _, p = oracle.attend(q, k, v, ivs, 0.25, want_probs=True)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+
+
+def test_empty_row_outputs_zero():
+    q, k, v = _rand((3, 1, 8), 7), _rand((5, 1, 8), 8), _rand((5, 1, 8), 9)
+    out = oracle.attend(q, k, v, [[], [(0, 5)], []], 1.0)
+    assert np.all(out[0] == 0) and np.all(out[2] == 0) and np.any(out[1] != 0)
+
+
+def test_bf16_inputs_widen_exactly():
+    x = np.array([1.0, -2.5, 3.140625, 1e-3], dtype=np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    w = oracle.widen(b)
+    assert w.dtype == np.float32
+    np.testing.assert_array_equal(w[:3], x[:3])
+    assert abs(w[3] - 1e-3) < 1e-5
+
+
+# ---------------------------------------------------------------------------------------------
+# closed forms (C1-C4)
+# ---------------------------------------------------------------------------------------------
+
+def test_zero_query_gives_mean_of_allowed_values():
+    """C1: q = 0 makes every allowed score equal, so the output is the mean of the allowed v."""
+    k, v = _rand((20, 2, 8), 10), _rand((20, 2, 8), 11)
+    q = np.zeros((2, 2, 8), np.float32)
+    ivs = [[(3, 9), (15, 20)], [(0, 20)]]
+    out = oracle.attend(q, k, v, ivs, 0.5)
+    np.testing.assert_allclose(out[0], np.concatenate([v[3:9], v[15:20]]).astype(np.float64).mean(0), atol=1e-12)
+    np.testing.assert_allclose(out[1], v.astype(np.float64).mean(0), atol=1e-12)
+
+
+def test_equal_keys_give_mean_of_values():
+    """C2: identical keys make the weights uniform whatever q is."""
+    q, v = _rand((4, 1, 16), 12), _rand((10, 1, 16), 13)
+    k = np.repeat(_rand((1, 1, 16), 14), 10, axis=0)
+    out = oracle.attend(q, k, v, [[(0, 10)]] * 4, 0.3)
+    np.testing.assert_allclose(out, np.broadcast_to(v.astype(np.float64).mean(0), out.shape), atol=1e-12)
+
+
+def test_dominant_logit_selects_its_value():
+    """C3: a key whose logit exceeds all others by 40 takes weight 1 - O(e^-40)."""
+    D = 4
+    q = np.zeros((1, 1, D), np.float32)
+    q[0, 0, 0] = 1.0
+    k = np.zeros((9, 1, D), np.float32)
+    k[5, 0, 0] = 40.0
+    v = _rand((9, 1, D), 15)
+    out = oracle.attend(q, k, v, [[(0, 9)]], 1.0)
+    np.testing.assert_allclose(out[0, 0], v[5, 0], atol=1e-6)
+
+
+def test_constant_values_pass_through():
+    """C4: when every allowed v is the same vector, so is the output."""
+    q, k = _rand((6, 3, 8), 16), _rand((25, 3, 8), 17)
+    c = _rand((1, 3, 8), 18)
+    v = np.repeat(c, 25, axis=0)
+    out = oracle.attend(q, k, v, [[(i, 25)] for i in range(6)], 0.7)
+    np.testing.assert_allclose(out, np.broadcast_to(c.astype(np.float64), out.shape), atol=1e-12)
+
+
+def test_linear_in_values():
+    """I6: for fixed q and k the output is linear in V."""
+    q, k = _rand((5, 2, 8), 19), _rand((13, 2, 8), 20)
+    v1, v2 = _rand((13, 2, 8), 21), _rand((13, 2, 8), 22)
+    ivs = [[(0, 13)], [(2, 7)], [(0, 1), (5, 13)], [(12, 13)], [(0, 13)]]
+    a, b = 0.75, -1.5
+    lhs = oracle.attend(q, k, (a * v1 + b * v2).astype(np.float32), ivs, 0.4)
+    rhs = a * oracle.attend(q, k, v1, ivs, 0.4) + b * oracle.attend(q, k, v2, ivs, 0.4)
+    np.testing.assert_allclose(lhs, rhs, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------------------------
+# cache policy: loop simulation, layout, traces
+# ---------------------------------------------------------------------------------------------
+
+def loop_simulation(S, W, n_frames_total, per_append):
+    """The repo-explainer loop at frame granularity: the state list keeps the anchor
+    frames and, after each append, drops the oldest non-anchor frames beyond W."""
+    state, anchors, history = [], [], []
+    f = 0
+    while f < n_frames_total:
+        for _ in range(min(per_append, n_frames_total - f)):
+            state.append(f)
+            if len(anchors) < S:
+                anchors.append(f)
+            f += 1
+        while len([x for x in state if x not in anchors]) > W:
+            oldest = min(x for x in state if x not in anchors)
+            state.remove(oldest)
+        history.append((f, list(state)))
+    return history
+
+
+@pytest.mark.parametrize("S,W,cf", [(6, 8, 4), (1, 2, 2), (0, 3, 1), (2, 5, 3), (3, 1, 2), (4, 4, 4)])
+def test_resident_set_matches_loop_simulation(S, W, cf):
+    """I4: after every append the sinks are frames 0..S-1 and the rest are the last W frames."""
+    for F, state in loop_simulation(S, W, 40, cf):
+        assert oracle.resident_frames(F, S, W) == sorted(state)
+        assert oracle.valid_slots(F, S, W) == len(state)
+
+
+@pytest.mark.parametrize("S,W,cf", [(6, 8, 4), (1, 2, 2), (0, 3, 1), (2, 5, 3), (3, 1, 2), (5, 3, 7)])
+def test_resident_frames_fill_slot_prefix(S, W, cf):
+    """I5: resident frames always occupy slots 0..valid-1, one frame per slot."""
+    for F in range(0, 60):
+        slots = sorted(oracle.slot_of_frame(f, S, W) for f in oracle.resident_frames(F, S, W))
+        assert slots == list(range(oracle.valid_slots(F, S, W)))
+
+
+def test_long_append_keeps_last_window_frames():
+    """An append longer than the window leaves the same resident set as appending its
+    frames one by one; the skipped frames are exactly the ones the loop would evict."""
+    S, W, tpf, H, D = 2, 3, 2, 1, 4
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    rows = _rand((9 * tpf, H, D), 23)
+    cm.append(rows, -rows, 9)
+    assert cm.resident() == [0, 1, 6, 7, 8]
+    assert oracle.frames_kept_by_append(0, 9, S, W) == [0, 1, 6, 7, 8]
+    kb, vb = cm.slot_buffers()
+    for f in cm.resident():
+        s = oracle.slot_of_frame(f, S, W)
+        np.testing.assert_array_equal(kb[s], rows[f * tpf:(f + 1) * tpf])
+        np.testing.assert_array_equal(vb[s], -rows[f * tpf:(f + 1) * tpf])
+
+
+def test_traces_match_hand_derivation():
+    g = _golden("cache_traces.json")
+    t = g["tiny_rollout"]
+    S, W, cf = t["sink_frames"], t["window_frames"], t["chunk_frames"]
+    cm = oracle.CacheModel(S, W, 1, 1, 1, dtype=np.float32)
+    for c, want in enumerate(t["resident_before_chunk"]):
+        assert cm.resident() == want
+        cm.append(np.zeros((cf, 1, 1), np.float32), np.zeros((cf, 1, 1), np.float32), cf)
+    assert cm.slot_map().tolist() == t["slot_map_after_6_chunks"]
+
+    t = g["rolling_832x464"]
+    S, W, cf = t["sink_frames"], t["window_frames"], t["chunk_frames"]
+    cm = oracle.CacheModel(S, W, 1, 1, 1, dtype=np.float32)
+    z = np.zeros((cf, 1, 1), np.float32)
+    for c in range(8):
+        if c < len(t["valid_slots_before_chunk"]):
+            assert oracle.valid_slots(cm.F, S, W) == t["valid_slots_before_chunk"][c]
+        if c == 4:
+            assert cm.slot_map().tolist() == t["slot_map_before_chunk_4"]
+        if c == 5:
+            assert cm.slot_map().tolist() == t["slot_map_before_chunk_5"]
+        cm.append(z, z, cf)
+    assert cm.F == 32
+    assert cm.slot_map().tolist() == t["slot_map_after_32_frames"]
+
+
+def test_eighteen_slot_layout():
+    """6 anchors + 8 recent + 4 current frames once the 832x464 session is past chunk 3."""
+    g = _golden("layout_18slot.json")
+    S, W, cf, tpf = g["anchor_frames"], g["recent_frames"], g["current_frames"], g["tokens_per_frame"]
+    for F in range(16, 16 + 4 * 50, 4):
+        res = oracle.resident_frames(F, S, W)
+        assert len([f for f in res if f < S]) == S
+        assert len([f for f in res if f >= S]) == W
+        assert len(res) + cf == g["total_slots"]
+        assert len(res) * tpf == g["cache_tokens"]
+        assert (len(res) + cf) * tpf == g["kv_tokens"]
+        assert cf * tpf == g["q_tokens"]
+
+
+def test_cache_model_contents_by_slot():
+    """P4: a slot holds exactly the rows of the append call that carried its frame."""
+    S, W, cf, tpf, H, D = 2, 3, 2, 3, 2, 4
+    cm = oracle.CacheModel(S, W, tpf, H, D)
+    sent = {}
+    for c in range(7):
+        kb = synth.normal(cf * tpf * H * D, seed=5, chunk=c, kind=synth.KFIN).reshape(cf * tpf, H, D)
+        vb = synth.normal(cf * tpf * H * D, seed=5, chunk=c, kind=synth.VFIN).reshape(cf * tpf, H, D)
+        for j in range(cf):
+            sent[c * cf + j] = (kb[j * tpf:(j + 1) * tpf], vb[j * tpf:(j + 1) * tpf])
+        cm.append(kb, vb, cf)
+        kbuf, vbuf = cm.slot_buffers()
+        for s, f in enumerate(cm.slot_map()):
+            if f >= 0:
+                np.testing.assert_array_equal(kbuf[s], sent[f][0])
+                np.testing.assert_array_equal(vbuf[s], sent[f][1])
+            else:
+                assert s >= oracle.valid_slots(cm.F, S, W)
+
+
+# ---------------------------------------------------------------------------------------------
+# rollout: incremental cache attention vs one dense masked softmax (tiny workload, fp32)
+# ---------------------------------------------------------------------------------------------
+
+def rollout_allowed(fq, fk, S, W, cf):
+    """Frame-level mask of the whole tiny rollout: a query frame sees its own chunk
+    (both directions) and, among earlier chunks' frames, the sinks and the last W."""
+    cq, ck = fq // cf, fk // cf
+    Fq = cq * cf
+    return (ck == cq) or (fk < Fq and (fk < S or fk >= Fq - W))
+
+
+def _tiny_rollout(S, W, cf, tpf, H, D, n_chunks, seed):
+    """Run the oracle chunk by chunk (current chunk's K/V as the segment, then append it)
+    and return (all q, all k, all v, outputs), each stacked over the whole sequence."""
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    n = cf * tpf * H * D
+    qs, ks, vs, outs = [], [], [], []
+    for c in range(n_chunks):
+        q = synth.normal(n, dtype="f32", seed=seed, chunk=c, kind=synth.Q).reshape(cf * tpf, H, D)
+        k = synth.normal(n, dtype="f32", seed=seed, chunk=c, kind=synth.K).reshape(cf * tpf, H, D)
+        v = synth.normal(n, dtype="f32", seed=seed, chunk=c, kind=synth.V).reshape(cf * tpf, H, D)
+        outs.append(oracle.chunk_attention(cm, q, [(k, v)], 1.0 / np.sqrt(D)))
+        cm.append(k, v, cf)
+        qs.append(q), ks.append(k), vs.append(v)
+    return np.concatenate(qs), np.concatenate(ks), np.concatenate(vs), np.concatenate(outs)
+
+
+def _dense_rollout_mask(S, W, cf, tpf, n_frames):
+    fr = np.arange(n_frames * tpf) // tpf
+    return np.array([[rollout_allowed(a, b, S, W, cf) for b in fr] for a in fr])
+
+
+def test_tiny_rollout_matches_dense_masked_softmax():
+    """The tiny fp32 workload verbatim: 1 head, head_dim 64, 16 tokens per frame,
+    chunks of 2 frames, 1 sink + window 2, 6 chunks, checked against one dense mask."""
+    S, W, cf, tpf, H, D, n = 1, 2, 2, 16, 1, 64, 6
+    q, k, v, out = _tiny_rollout(S, W, cf, tpf, H, D, n, seed=0)
+    ref, _ = dense_masked_softmax(q, k, v, _dense_rollout_mask(S, W, cf, tpf, n * cf), 1.0 / np.sqrt(D))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("S,W,cf", [(1, 10, 2), (0, 12, 3), (4, 8, 4)])
+def test_full_window_rollout_is_block_causal(S, W, cf):
+    """I2: when S + W covers all history, the rollout equals full-sequence block-causal attention."""
+    tpf, H, D, n = 3, 2, 8, 4
+    assert S + W >= cf * (n - 1)          # every earlier chunk stays resident
+    q, k, v, out = _tiny_rollout(S, W, cf, tpf, H, D, n, seed=1)
+    fr = np.arange(n * cf * tpf) // (cf * tpf)
+    mask = fr[None, :] <= fr[:, None]
+    ref, _ = dense_masked_softmax(q, k, v, mask, 1.0 / np.sqrt(D))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_permuting_current_chunk_permutes_outputs():
+    """I3: permuting the current chunk's tokens (q rows with their k/v rows) permutes outputs."""
+    S, W, cf, tpf, H, D = 2, 3, 2, 5, 2, 16
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    for c in range(3):
+        cm.append(_rand((cf * tpf, H, D), 30 + c), _rand((cf * tpf, H, D), 40 + c), cf)
+    q, k, v = _rand((cf * tpf, H, D), 50), _rand((cf * tpf, H, D), 51), _rand((cf * tpf, H, D), 52)
+    perm = np.random.default_rng(3).permutation(cf * tpf)
+    a = oracle.chunk_attention(cm, q, [(k, v)], 0.3)
+    b = oracle.chunk_attention(cm, q[perm], [(k[perm], v[perm])], 0.3)
+    np.testing.assert_allclose(b, a[perm], atol=1e-12)
+
+
+def test_chunk_attention_rows_subset():
+    S, W, cf, tpf, H, D = 1, 2, 2, 4, 3, 8
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    cm.append(_rand((cf * tpf, H, D), 60), _rand((cf * tpf, H, D), 61), cf)
+    q, k, v = _rand((cf * tpf, H, D), 62), _rand((cf * tpf, H, D), 63), _rand((cf * tpf, H, D), 64)
+    full = oracle.chunk_attention(cm, q, [(k, v)], 0.5)
+    rows = [7, 0, 3]
+    np.testing.assert_array_equal(oracle.chunk_attention(cm, q, [(k, v)], 0.5, rows=rows), full[rows])
+
+
+# ---------------------------------------------------------------------------------------------
+# MoBA mask
+# ---------------------------------------------------------------------------------------------
+
+def moba_pair_allowed(i, j, tpf, frames, cf):
+    """M1-M4 stated pairwise: clean->clean if key chunk <= query chunk; noisy->clean if
+    key chunk < query chunk; noisy->noisy if same chunk; block->block always."""
+    L = frames * tpf
+    pi, pj = i // L, j // L
+    ki, kj = ((i % L) // tpf) // cf, ((j % L) // tpf) // cf
+    if pi == 0 and pj == 0:
+        return kj <= ki
+    if pi == 1 and pj == 0:
+        return kj < ki
+    if pi == 1 and pj == 1:
+        return kj == ki
+    if pi == 2 and pj == 2:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("tpf,frames,cf", [(4, 6, 2), (3, 7, 3), (2, 5, 1), (5, 4, 4), (1, 9, 2)])
+def test_moba_intervals_match_pairwise_mask(tpf, frames, cf):
+    n = 3 * frames * tpf
+    want = np.array([[moba_pair_allowed(i, j, tpf, frames, cf) for j in range(n)] for i in range(n)])
+    ivs = [oracle.moba_row_intervals(i, tpf, frames, cf) for i in range(n)]
+    np.testing.assert_array_equal(mask_from_intervals(ivs, n), want)
+
+
+def test_moba_tiny_matches_dense_brute_force():
+    tpf, frames, cf, H, D = 4, 6, 2, 2, 16
+    n = 3 * frames * tpf
+    q, k, v = _rand((n, H, D), 70), _rand((n, H, D), 71), _rand((n, H, D), 72)
+    mask = np.array([[moba_pair_allowed(i, j, tpf, frames, cf) for j in range(n)] for i in range(n)])
+    ref, _ = dense_masked_softmax(q, k, v, mask, 0.25)
+    out = oracle.moba_attention(q, k, v, tpf, frames, cf, 1, 0.25)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+def test_moba_allowed_pair_count_at_full_size():
+    """945 of 3969 frame pairs (23.8 %) for 21+21+21 frames in chunks of 3, at 1560 tokens per frame."""
+    g = _golden("moba_pairs.json")
+    tpf, frames, cf = 1560, g["frames"], g["chunk_frames"]
+    total = 0
+    for i in range(0, 3 * frames * tpf, tpf):       # one row per frame: every row of a frame has the same mask
+        total += sum(b - a for a, b in oracle.moba_row_intervals(i, tpf, frames, cf)) * tpf
+    assert total == g["allowed_frame_pairs"] * tpf * tpf
+    assert g["clean_clean"] + g["noisy_clean"] + g["noisy_noisy"] + g["block_block"] == g["allowed_frame_pairs"]
+    assert (3 * frames) ** 2 == g["total_frame_pairs"]
+
+
+def test_moba_noisy_rows_equal_teacher_forced_chunk_attention():
+    """I7: noisy chunk i = chunk attention over a cache holding clean chunks < i (no
+    eviction) with noisy chunk i as the current chunk."""
+    tpf, frames, cf, H, D = 3, 6, 2, 2, 8
+    L = frames * tpf
+    n = 3 * L
+    q, k, v = _rand((n, H, D), 80), _rand((n, H, D), 81), _rand((n, H, D), 82)
+    moba = oracle.moba_attention(q, k, v, tpf, frames, cf, 1, 0.3)
+    cl = cf * tpf
+    for c in range(frames // cf):
+        cm = oracle.CacheModel(0, frames, tpf, H, D, dtype=np.float32)
+        if c > 0:
+            cm.append(k[:c * cl], v[:c * cl], c * cf)
+        rows = slice(L + c * cl, L + (c + 1) * cl)
+        got = oracle.chunk_attention(cm, q[rows], [(k[rows], v[rows])], 0.3)
+        np.testing.assert_allclose(moba[rows], got, atol=1e-12)
+
+
+def test_moba_clean_rows_equal_block_causal_chunk_attention():
+    """Clean chunk i = chunk attention over a cache of clean chunks < i plus clean chunk i."""
+    tpf, frames, cf, H, D = 2, 6, 3, 1, 8
+    L = frames * tpf
+    q, k, v = _rand((3 * L, H, D), 83), _rand((3 * L, H, D), 84), _rand((3 * L, H, D), 85)
+    moba = oracle.moba_attention(q, k, v, tpf, frames, cf, 1, 0.6)
+    cl = cf * tpf
+    for c in range(frames // cf):
+        cm = oracle.CacheModel(0, frames, tpf, H, D, dtype=np.float32)
+        if c > 0:
+            cm.append(k[:c * cl], v[:c * cl], c * cf)
+        rows = slice(c * cl, (c + 1) * cl)
+        np.testing.assert_allclose(moba[rows], oracle.chunk_attention(cm, q[rows], [(k[rows], v[rows])], 0.6),
+                                   atol=1e-12)
+
+
+def test_moba_block_rows_equal_plain_bidirectional_attention():
+    """I8: rows of the appended block equal dense attention over the block alone."""
+    tpf, frames, cf, H, D = 3, 5, 2, 2, 8
+    L = frames * tpf
+    q, k, v = _rand((3 * L, H, D), 86), _rand((3 * L, H, D), 87), _rand((3 * L, H, D), 88)
+    moba = oracle.moba_attention(q, k, v, tpf, frames, cf, 1, 0.45)
+    B = slice(2 * L, 3 * L)
+    ref, _ = dense_masked_softmax(q[B], k[B], v[B], np.ones((L, L), bool), 0.45)
+    np.testing.assert_allclose(moba[B], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# chunk-wise causal cross-attention
+# ---------------------------------------------------------------------------------------------
+
+def test_cross_attention_ignores_other_chunks_prompts():
+    """I9: chunk i's output does not change when another chunk's local prompt changes."""
+    H, D, ne, nl, nc = 2, 16, 7, 5, 4
+    q = _rand((6, H, D), 90)
+    ke, ve = _rand((ne, H, D), 91), _rand((ne, H, D), 92)
+    kl = [_rand((nl, H, D), 100 + j) for j in range(nc)]
+    vl = [_rand((nl, H, D), 200 + j) for j in range(nc)]
+    a = oracle.cross_attention(q, 2, ke, ve, kl, vl, 0.25)
+    kl2 = [x if j == 2 else x * 3 + 1 for j, x in enumerate(kl)]
+    vl2 = [x if j == 2 else -x for j, x in enumerate(vl)]
+    b = oracle.cross_attention(q, 2, ke, ve, kl2, vl2, 0.25)
+    np.testing.assert_array_equal(a, b)
+    c = oracle.chunk_attention(None, q, [(ke, ve), (kl[2], vl[2])], 0.25)
+    np.testing.assert_allclose(a, c, atol=1e-12)
+    allk = np.concatenate([ke] + kl)
+    allv = np.concatenate([ve] + vl)
+    m = np.zeros((6, allk.shape[0]), bool)
+    m[:, :ne] = True
+    m[:, ne + 2 * nl: ne + 3 * nl] = True
+    ref, _ = dense_masked_softmax(q, allk, allv, m, 0.25)
+    np.testing.assert_allclose(a, ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# input generator
+# ---------------------------------------------------------------------------------------------
+
+def test_generator_known_answers():
+    """Philox4x32-10 known-answer vectors of the Random123 distribution."""
+    kats = [((0, 0, 0, 0), (0, 0), (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+            ((0xffffffff,) * 4, (0xffffffff, 0xffffffff), (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+            ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+             (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1))]
+    for ctr, key, want in kats:
+        got = synth.philox4x32_10_np([np.array([c]) for c in ctr], key)
+        assert [int(x[0]) for x in got] == list(want)
+        assert synth.philox4x32_10_c(ctr, key).tolist() == list(want)
+
+
+def test_generator_c_matches_numpy_and_moments():
+    for kind in range(9):
+        a = synth.normal_np(20000, seed=11, chunk=3, layer=7, step=2, kind=kind, start=1 << 33)
+        b = synth.normal(20000, dtype="f32", seed=11, chunk=3, layer=7, step=2, kind=kind, start=1 << 33)
+        np.testing.assert_array_equal(a, b)
+        bb = synth.normal(20000, dtype="bf16", seed=11, chunk=3, layer=7, step=2, kind=kind, start=1 << 33)
+        np.testing.assert_array_equal(bb, synth.f32_to_bf16_bits(a))
+    x = synth.normal(1 << 20, dtype="f32", seed=0)
+    assert abs(x.mean()) < 5e-3 and abs(x.var() - 65535 / 65536) < 5e-3
+    assert x.min() >= -1530 / 256 and x.max() <= 1530 / 256
