@@ -1,0 +1,182 @@
+/*
+ * wmk -- sink + window KV-cache chunk attention for MI355X (gfx950).
+ *
+ * The hot path of a causal video DiT that generates latent-video chunks one
+ * after another from cached history plus current inputs ("Mix Forcing: Causal
+ * Pre-Training via Mixture Attention for Interactive World Models", Overview).
+ * Per DiT layer the cache keeps the first frames as anchors ("sinks") for good
+ * and a sliding window of the most recently finalized frames, evicting older
+ * non-sink frames ("LingBot-World-Infinity: The Open-Source World Model That
+ * Refuses to Forget", "The trick: treat video like a causal stream" and "How the
+ * cache keeps the world alive").  The queries of the current chunk attend the
+ * resident frames and the chunk itself -- 6 anchors + 8 recent + 4 current = 18
+ * latent-frame slots in the native model ("Westlake AGI Lab's 'World in World'
+ * Steers Frozen Video Models", second paragraph).  Training uses the MoBA mask:
+ * a teacher-forcing mask plus an appended, fully bidirectional block
+ * ("Infinite Worlds with Versatile Interactions", causal pretraining paragraph).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Token tensors are row-major [tokens][heads][head_dim], batch 1, in the
+ *   dtype named by the descriptor (bf16 or fp32).  Softmax and accumulation are
+ *   fp32 inside the kernels; bf16 outputs are rounded to nearest-even.
+ * - All tensor pointers are device pointers owned by the caller and must be
+ *   16-byte aligned.  The library never allocates or frees device memory and
+ *   never synchronizes the device or a stream.
+ * - Every call that does GPU work only enqueues it on the given stream and
+ *   returns.  Calls on one cache must be issued on one stream (or ordered by
+ *   the caller); host-side counters advance when the work is enqueued.
+ * - On any error nothing is enqueued, no state changes, and a message is
+ *   available from wmk_last_error() on the calling thread.
+ */
+#ifndef WMK_H
+#define WMK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WMK_OK = 0,
+    WMK_ERR_NULL = 1,     /* a required pointer is NULL                              */
+    WMK_ERR_SHAPE = 2,    /* a size, count or shape is out of its allowed set         */
+    WMK_ERR_DTYPE = 3,    /* unsupported dtype, or dtype differs from the cache's     */
+    WMK_ERR_RANGE = 4,    /* layer index or scale out of range                        */
+    WMK_ERR_ALIGN = 5,    /* a device pointer is not 16-byte aligned                  */
+    WMK_ERR_CAPACITY = 6, /* caller-provided buffer too small                         */
+    WMK_ERR_HIP = 7       /* the HIP runtime refused a launch                         */
+} wmk_status;
+
+typedef enum { WMK_F32 = 0, WMK_BF16 = 1 } wmk_dtype;
+
+/* Shape of a per-layer KV cache.  Sinks and window are counted in latent
+ * frames; the window holds finalized non-sink frames and does not include the
+ * chunk being generated. */
+typedef struct {
+    int32_t num_layers;       /* >= 1                                                  */
+    int32_t num_heads;        /* >= 1                                                  */
+    int32_t head_dim;         /* 64 or 128                                             */
+    int32_t tokens_per_frame; /* >= 1 (1508 for a 52x29 latent grid)                   */
+    int32_t sink_frames;      /* S >= 0                                                */
+    int32_t window_frames;    /* W >= 1                                                */
+    int32_t chunk_frames;     /* frames per finalized chunk; >= 1 (informational)      */
+    wmk_dtype dtype;          /* element type of K and V; stored bit-exactly           */
+} wmk_cache_desc;
+
+typedef struct wmk_cache wmk_cache; /* opaque host handle */
+
+typedef struct {
+    int32_t num_heads;
+    int32_t head_dim; /* 64 or 128 */
+    wmk_dtype dtype;
+} wmk_head_desc;
+
+/* An extra span of keys/values, [tokens][heads][head_dim] each: the current
+ * chunk's own K/V at a chunk step, or prompt K/V for cross-attention. */
+typedef struct {
+    const void* k;
+    const void* v;
+    int32_t tokens; /* >= 1 */
+} wmk_kv_segment;
+
+/* MoBA training sequence: [clean | noisy | bidirectional block], each part
+ * `frames` latent frames of `tokens_per_frame` tokens; chunks of
+ * `chunk_frames` frames (the last chunk of a part may be shorter). */
+typedef struct {
+    int32_t tokens_per_frame; /* >= 1 */
+    int32_t frames;           /* >= 1, frames per part */
+    int32_t chunk_frames;     /* >= 1 */
+    int32_t bidir_block;      /* 1: append the bidirectional block; 0: clean + noisy only */
+} wmk_moba_desc;
+
+/* Bytes of the K buffer (equal to the V buffer) for all layers of a cache with
+ * descriptor d: num_layers * (S + W) * tokens_per_frame * heads * head_dim *
+ * sizeof(dtype).  Layout [layer][slot][tokens_per_frame][heads][head_dim].
+ * Returns 0 when d is NULL or invalid. */
+size_t wmk_cache_bytes(const wmk_cache_desc* d);
+
+/* Create a cache handle over caller-allocated K and V buffers of at least
+ * capacity_bytes each (>= wmk_cache_bytes(d)).  Host-only: validates and
+ * records the descriptor and sets every layer's frame counter to zero; the
+ * buffers' contents are not touched (unfilled slots are never read).
+ * Cache policy: sinks, then a window of W recent frames ("How the cache keeps
+ * the world alive"); 18-slot layout of "World in World".
+ * Errors: NULL d/k_dev/v_dev/out -> WMK_ERR_NULL; invalid descriptor ->
+ * WMK_ERR_SHAPE or WMK_ERR_DTYPE; misaligned buffer -> WMK_ERR_ALIGN;
+ * capacity_bytes too small -> WMK_ERR_CAPACITY.  On error *out is untouched. */
+wmk_status wmk_cache_init(const wmk_cache_desc* d, void* k_dev, void* v_dev, size_t capacity_bytes,
+                          wmk_cache** out);
+
+/* Free the host handle (not the caller's buffers).  NULL is accepted. */
+void wmk_cache_destroy(wmk_cache* c);
+
+/* Append n_frames finalized frames to `layer` and evict in the same step.
+ * k_new and v_new are [n_frames * tokens_per_frame][heads][head_dim] in the
+ * cache dtype.  Frame f (global append order) lands in slot f if f < S, else
+ * in slot S + (f - S) mod W, overwriting -- and so evicting -- frame f - W.
+ * Frames that this same call would overwrite (only when n_frames > W) are not
+ * written.  Bits are copied exactly.  The frame counter advances on enqueue.
+ * Errors: NULL -> WMK_ERR_NULL; layer outside [0, num_layers) -> WMK_ERR_RANGE;
+ * n_frames <= 0 -> WMK_ERR_SHAPE; misaligned -> WMK_ERR_ALIGN; launch refused
+ * -> WMK_ERR_HIP (counter not advanced). */
+wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                                  int32_t n_frames, hipStream_t stream);
+
+/* Host-side view of a layer's slots: frame_of_slot[S + W] receives the frame
+ * held by each slot (-1 when empty) and *frames_appended the layer's counter
+ * (either output pointer may be NULL).  Resident frames always fill the slot
+ * prefix [0, valid).  No GPU work. */
+wmk_status wmk_cache_slots(const wmk_cache* c, int32_t layer, int64_t* frame_of_slot, int64_t* frames_appended);
+
+/* Bytes of optional scratch that lets the attention calls below split the last,
+ * partly filled round of work units over the whole GPU (a split-KV tail with an
+ * in-kernel merge).  Passing less (or NULL) is valid and only disables that
+ * split.  q_tokens and heads are those of the call. */
+size_t wmk_attention_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens);
+
+/* Chunk attention at a denoising step: every query row of the current chunk
+ * attends every resident frame of `layer` in cache c (if c is not NULL) and
+ * every token of the n_seg extra segments (the current chunk's own K/V --
+ * bidirectional inside the chunk -- or prompt K/V for cross-attention, where
+ * chunk i passes the shared environment prompt and its own local prompt only,
+ * "Mix Forcing", "Condition each chunk").  No other mask applies: every
+ * resident frame is in the past, and causality lives in which frames are
+ * resident.  out_i = softmax_j(scale * q_i . k_j) v_j per head.
+ * q and out: [q_tokens][heads][head_dim], dtype of hd.  A row with no key at
+ * all (empty cache and n_seg = 0) gets zeros.
+ * Errors: NULL hd/q/out, or NULL seg with n_seg > 0 -> WMK_ERR_NULL; head_dim
+ * not 64/128, q_tokens <= 0, n_seg outside [0, 4], a segment with tokens <= 0,
+ * more than 2^31 - 1 keys, or hd not matching the cache -> WMK_ERR_SHAPE;
+ * dtype -> WMK_ERR_DTYPE; layer out of range or scale not finite and > 0 ->
+ * WMK_ERR_RANGE; misaligned -> WMK_ERR_ALIGN; launch refused -> WMK_ERR_HIP. */
+wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
+                               int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* MoBA-masked attention forward over one training sequence
+ * [clean | noisy | block] ("Infinite Worlds with Versatile Interactions",
+ * causal pretraining paragraph; "Mix Forcing", "Mix the training modes").
+ * With k = chunk index of a token inside its part: clean rows see clean keys
+ * of chunks <= k; noisy rows see clean keys of chunks < k and noisy keys of
+ * chunk k; block rows see the whole block; nothing else is allowed.
+ * q, k, v and out are [(2 + bidir_block) * frames * tokens_per_frame][heads]
+ * [head_dim] in the dtype of hd.  Errors as for wmk_chunk_attention, plus
+ * bidir_block outside {0, 1} or a non-positive field -> WMK_ERR_SHAPE. */
+wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
+                              const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Message of the last error on the calling thread ("" if none); valid until
+ * the next wmk call on that thread. */
+const char* wmk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WMK_H */

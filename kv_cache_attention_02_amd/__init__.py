@@ -1,0 +1,232 @@
+"""wmk -- sink + window KV-cache chunk attention for MI355X (gfx950).
+
+Python binding of the C ABI in ``include/wmk.h`` (``libwmk.so``, built in place
+by :func:`kv_cache_attention_02_amd.build.build`).  The functions named
+``wmk_*`` are the C entry points themselves, loaded with ctypes; the helpers
+below them (:class:`Cache`, :func:`chunk_attention`, :func:`moba_attention`)
+only marshal torch tensors into pointers, sizes and the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback path: if ``libwmk.so`` is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_DIR, "libwmk.so")
+
+WMK_OK, WMK_ERR_NULL, WMK_ERR_SHAPE, WMK_ERR_DTYPE, WMK_ERR_RANGE, WMK_ERR_ALIGN, WMK_ERR_CAPACITY, WMK_ERR_HIP = \
+    range(8)
+STATUS_NAMES = {0: "WMK_OK", 1: "WMK_ERR_NULL", 2: "WMK_ERR_SHAPE", 3: "WMK_ERR_DTYPE", 4: "WMK_ERR_RANGE",
+                5: "WMK_ERR_ALIGN", 6: "WMK_ERR_CAPACITY", 7: "WMK_ERR_HIP"}
+WMK_F32, WMK_BF16 = 0, 1
+MAX_SEGMENTS = 4
+
+
+class wmk_cache_desc(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("tokens_per_frame", ctypes.c_int32), ("sink_frames", ctypes.c_int32),
+                ("window_frames", ctypes.c_int32), ("chunk_frames", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class wmk_head_desc(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class wmk_kv_segment(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("tokens", ctypes.c_int32)]
+
+
+class wmk_moba_desc(ctypes.Structure):
+    _fields_ = [("tokens_per_frame", ctypes.c_int32), ("frames", ctypes.c_int32), ("chunk_frames", ctypes.c_int32),
+                ("bidir_block", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "wmk_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_cache_desc)]),
+    "wmk_cache_init": (ctypes.c_int, [ctypes.POINTER(wmk_cache_desc), _P, _P, ctypes.c_size_t, ctypes.POINTER(_P)]),
+    "wmk_cache_destroy": (None, [_P]),
+    "wmk_cache_append_evict": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
+    "wmk_cache_slots": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64)]),
+    "wmk_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_head_desc), ctypes.c_int32]),
+    "wmk_chunk_attention": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
+                                           ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P, ctypes.c_float, _P,
+                                           ctypes.c_size_t, _P]),
+    "wmk_moba_attention": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P, _P, _P,
+                                          _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "wmk_last_error": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+def load():
+    """Load libwmk.so (raises if it is not built) and return the ctypes handle."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                               "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def __getattr__(name):  # wmk_* entry points resolve to the loaded C functions
+    if name in _SIGNATURES:
+        return getattr(load(), name)
+    raise AttributeError(name)
+
+
+class WmkError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+def _check(status):
+    if status != WMK_OK:
+        raise WmkError(status, load().wmk_last_error().decode())
+
+
+# ----------------------------------------------------------------------------------------------
+# torch marshalling helpers
+# ----------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t == torch.bfloat16:
+        return WMK_BF16
+    if t == torch.float32:
+        return WMK_F32
+    raise TypeError(f"unsupported dtype {t} (bfloat16 or float32)")
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+_workspaces = {}
+
+
+def workspace(device, nbytes):
+    """A per-device scratch buffer of at least nbytes (grown on demand, kept for reuse)."""
+    torch = _torch()
+    dev = torch.device(device)
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
+
+
+class Cache:
+    """A per-layer sink + window KV cache over torch-allocated K/V buffers.
+
+    Buffers are [num_layers][S + W][tokens_per_frame][heads][head_dim] each,
+    allocated here through torch (the library itself never allocates).
+    """
+
+    def __init__(self, *, num_layers, num_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
+                 chunk_frames, dtype=None, device="cuda"):
+        torch = _torch()
+        dtype = torch.bfloat16 if dtype is None else dtype
+        self.desc = wmk_cache_desc(num_layers, num_heads, head_dim, tokens_per_frame, sink_frames, window_frames,
+                                   chunk_frames, _dtype_code(dtype))
+        nbytes = load().wmk_cache_bytes(ctypes.byref(self.desc))
+        if nbytes == 0:
+            raise WmkError(WMK_ERR_SHAPE, "invalid cache descriptor: " + load().wmk_last_error().decode())
+        shape = (num_layers, sink_frames + window_frames, tokens_per_frame, num_heads, head_dim)
+        self.k = torch.empty(shape, dtype=dtype, device=device)
+        self.v = torch.empty(shape, dtype=dtype, device=device)
+        self.dtype = dtype
+        self._h = ctypes.c_void_p()
+        _check(load().wmk_cache_init(ctypes.byref(self.desc), _ptr(self.k), _ptr(self.v), nbytes,
+                                     ctypes.byref(self._h)))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def append_evict(self, layer, k_new, v_new, n_frames=None, stream=None):
+        if n_frames is None:
+            n_frames = k_new.shape[0] // self.desc.tokens_per_frame
+        _check(load().wmk_cache_append_evict(self._h, layer, _ptr(k_new), _ptr(v_new), n_frames,
+                                             _stream_ptr(stream)))
+
+    def slots(self, layer):
+        n = self.desc.sink_frames + self.desc.window_frames
+        arr = (ctypes.c_int64 * n)()
+        F = ctypes.c_int64()
+        _check(load().wmk_cache_slots(self._h, layer, arr, ctypes.byref(F)))
+        return list(arr), F.value
+
+    def close(self):
+        if self._h:
+            load().wmk_cache_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_workspace=True, stream=None):
+    """out[q_tokens][H][D] = attention of q over the resident frames of `layer` in `cache`
+    (None for none) and every token of `segments` (a list of (k, v) tensors)."""
+    torch = _torch()
+    nq, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    segs = (wmk_kv_segment * max(1, len(segments)))()
+    for i, (k, v) in enumerate(segments):
+        segs[i] = wmk_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[0])
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ws, wsb = ctypes.c_void_p(0), 0
+    if use_workspace:
+        wsb = load().wmk_attention_workspace_bytes(ctypes.byref(hd), nq)
+        if wsb:
+            w = workspace(q.device, wsb)
+            ws, wsb = _ptr(w), w.numel()
+    _check(load().wmk_chunk_attention(cache.handle if cache is not None else None, layer, ctypes.byref(hd), _ptr(q),
+                                      nq, segs, len(segments), _ptr(out), scale, ws, wsb, _stream_ptr(stream)))
+    return out
+
+
+def moba_attention(q, k, v, *, tokens_per_frame, frames, chunk_frames, bidir_block=1, out=None, scale=None,
+                   stream=None):
+    """MoBA-masked attention forward over [clean | noisy | block]."""
+    torch = _torch()
+    n, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    md = wmk_moba_desc(tokens_per_frame, frames, chunk_frames, bidir_block)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(load().wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                     scale, None, 0, _stream_ptr(stream)))
+    return out

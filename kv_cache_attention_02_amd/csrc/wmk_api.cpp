@@ -1,0 +1,496 @@
+// The C ABI of include/wmk.h: argument checks, host-side cache bookkeeping and
+// launch planning.  Bookkeeping is a per-layer frame counter on the host; it
+// decides slots and resident prefixes without ever reading the device, so a
+// generation loop needs no host/device synchronization (the per-layer host
+// syncs that the LingBot-World 2.0 speed-up write-up removes in its
+// step-ablation table, "Host syncs" row, do not arise).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "wmk.h"
+#include "wmk_internal.h"
+
+struct wmk_cache {
+    wmk_cache_desc d;
+    char* k;
+    char* v;
+    size_t frame_bytes;  // one latent frame of one layer: tpf * heads * head_dim * elem
+    size_t layer_bytes;  // (S + W) frames
+    std::vector<int64_t> frames;  // per layer: frames appended so far
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+wmk_status fail(wmk_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+wmk_status ok() {
+    g_err.clear();
+    return WMK_OK;
+}
+
+size_t elem_size(wmk_dtype t) { return t == WMK_F32 ? 4 : 2; }
+bool dtype_ok(int t) { return t == WMK_F32 || t == WMK_BF16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Test hook: WMK_FAULT_INJECT=1 makes every launch report a refused launch
+// before touching the device, so the no-state-change-on-error rule can be
+// checked on a machine without a GPU.
+bool fault_injected() {
+    const char* e = getenv("WMK_FAULT_INJECT");
+    return e != nullptr && e[0] == '1';
+}
+
+// Test hook: WMK_DRY_RUN=<path> checks and plans every call but launches
+// nothing; each planned launch is appended to <path> as one line, so host
+// bookkeeping and planning can be checked on a machine without a GPU.
+const char* dry_run_path() {
+    const char* e = getenv("WMK_DRY_RUN");
+    return (e != nullptr && e[0] != '\0') ? e : nullptr;
+}
+
+void dry_log(const char* fmt, ...) {
+    const char* path = dry_run_path();
+    if (path == nullptr) return;
+    FILE* f = fopen(path, "a");
+    if (f == nullptr) return;
+    va_list ap;
+    va_start(ap, fmt);
+    vfprintf(f, fmt, ap);
+    va_end(ap);
+    fclose(f);
+}
+
+wmk_status check_desc(const wmk_cache_desc* d) {
+    if (d == nullptr) return fail(WMK_ERR_NULL, "cache descriptor is NULL");
+    if (!dtype_ok(d->dtype)) return fail(WMK_ERR_DTYPE, "dtype %d is not WMK_F32 or WMK_BF16", (int)d->dtype);
+    if (d->num_layers < 1 || d->num_heads < 1 || d->tokens_per_frame < 1 || d->sink_frames < 0 ||
+        d->window_frames < 1 || d->chunk_frames < 1)
+        return fail(WMK_ERR_SHAPE, "cache descriptor has a non-positive field (layers %d heads %d tpf %d S %d W %d cf %d)",
+                    d->num_layers, d->num_heads, d->tokens_per_frame, d->sink_frames, d->window_frames,
+                    d->chunk_frames);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(WMK_ERR_SHAPE, "head_dim %d is not 64 or 128", d->head_dim);
+    const int64_t slots = (int64_t)d->sink_frames + d->window_frames;
+    if (slots * d->tokens_per_frame > INT32_MAX)
+        return fail(WMK_ERR_SHAPE, "(S + W) * tokens_per_frame exceeds 2^31 - 1 tokens");
+    return WMK_OK;
+}
+
+wmk_status check_head(const wmk_head_desc* hd) {
+    if (hd == nullptr) return fail(WMK_ERR_NULL, "head descriptor is NULL");
+    if (!dtype_ok(hd->dtype)) return fail(WMK_ERR_DTYPE, "dtype %d is not WMK_F32 or WMK_BF16", (int)hd->dtype);
+    if (hd->num_heads < 1) return fail(WMK_ERR_SHAPE, "num_heads %d < 1", hd->num_heads);
+    if (hd->head_dim != 64 && hd->head_dim != 128)
+        return fail(WMK_ERR_SHAPE, "head_dim %d is not 64 or 128", hd->head_dim);
+    return WMK_OK;
+}
+
+wmk_status check_scale(float scale) {
+    if (!(scale > 0.0f) || !isfinite(scale)) return fail(WMK_ERR_RANGE, "scale %g is not finite and > 0", scale);
+    return WMK_OK;
+}
+
+// Slot of frame f (first S frames: their own slot; later frames: ring of W).
+int64_t slot_of(const wmk_cache_desc& d, int64_t f) {
+    return f < d.sink_frames ? f : d.sink_frames + (f - d.sink_frames) % d.window_frames;
+}
+
+// Filled slots after F frames: they are always the prefix [0, valid).
+int64_t valid_of(const wmk_cache_desc& d, int64_t F) {
+    return std::min<int64_t>(F, d.sink_frames) + std::min<int64_t>(std::max<int64_t>(F - d.sink_frames, 0),
+                                                                    d.window_frames);
+}
+
+// ---- per-device facts used by the planner
+struct DeviceInfo {
+    int cus = 0;
+    int bpc64 = 0, bpc128 = 0;
+};
+std::mutex g_dev_mu;
+std::vector<DeviceInfo> g_dev;
+
+DeviceInfo device_info() {
+    if (dry_run_path() != nullptr) {  // no device: an MI355X-like 256 CUs, 2 workgroups each
+        DeviceInfo di;
+        di.cus = 256;
+        di.bpc64 = 2;
+        di.bpc128 = 2;
+        return di;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+    DeviceInfo& di = g_dev[dev];
+    if (di.cus == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        di.cus = cus;
+        di.bpc64 = wmk::attn_bf16_blocks_per_cu(64);
+        di.bpc128 = wmk::attn_bf16_blocks_per_cu(128);
+    }
+    return di;
+}
+
+constexpr int kBQ = 128, kBK = 64;
+constexpr int kMinTilesPerPiece = 8;
+
+// Split the last, partly filled round of units over the whole GPU when the
+// caller gave enough workspace.
+void plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws, size_t ws_bytes) {
+    p.split_units = 0;
+    p.splits = 1;
+    p.ws = nullptr;
+    if (ws == nullptr || tiles_per_unit < 2 * kMinTilesPerPiece) return;
+    const DeviceInfo di = device_info();
+    const int slots = di.cus * (head_dim == 64 ? di.bpc64 : di.bpc128);
+    if (slots <= 0) return;
+    const int32_t rounds = p.n_units / slots, tail = p.n_units % slots;
+    if (rounds < 1 || tail == 0) return;
+    int32_t splits = std::min<int32_t>(slots / tail, tiles_per_unit / kMinTilesPerPiece);
+    if (splits < 2) return;
+    if (wmk::attn_bf16_split_ws_bytes(head_dim, tail, splits) > ws_bytes) return;
+    p.split_units = tail;
+    p.splits = splits;
+    p.ws = ws;
+}
+
+// Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
+int32_t moba_qtile_cost(const wmk::MobaShape& m, int32_t q_tokens, int32_t qt) {
+    const int32_t r0 = qt * kBQ, r1 = std::min(r0 + kBQ, q_tokens);
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    std::vector<std::pair<int32_t, int32_t>> iv;
+    for (int32_t part = r0 / L; part <= (r1 - 1) / L && part < m.parts; ++part) {
+        const int32_t fa = std::max(r0, part * L) - part * L, fb = std::min(r1, (part + 1) * L) - part * L - 1;
+        const int32_t ka = fa / cl, kb = fb / cl;
+        if (part == 0) {
+            iv.push_back({0, std::min((kb + 1) * cl, L)});
+        } else if (part == 1) {
+            if (kb > 0) iv.push_back({0, kb * cl});
+            iv.push_back({L + ka * cl, L + std::min((kb + 1) * cl, L)});
+        } else {
+            iv.push_back({2 * L, 3 * L});
+        }
+    }
+    for (auto& x : iv) x = {x.first / kBK, (x.second + kBK - 1) / kBK};
+    std::sort(iv.begin(), iv.end());
+    int32_t total = 0, cur_b = -1, cur_e = -1;
+    for (auto& x : iv) {
+        if (x.second <= x.first) continue;
+        if (cur_e >= 0 && x.first <= cur_e) {
+            cur_e = std::max(cur_e, x.second);
+        } else {
+            if (cur_e >= 0) total += cur_e - cur_b;
+            cur_b = x.first;
+            cur_e = x.second;
+        }
+    }
+    if (cur_e >= 0) total += cur_e - cur_b;
+    return total;
+}
+
+// Longest-first launch order for MoBA: runs of consecutive q-tiles with equal
+// cost, sorted by decreasing cost.  Falls back to the natural order when there
+// are more runs than the kernel's table holds.
+void plan_moba_groups(wmk::AttnPlan& p, const wmk::MobaShape& m, int32_t q_tokens) {
+    struct Run { int32_t start, count, cost; };
+    std::vector<Run> runs;
+    for (int32_t qt = 0; qt < p.n_qtiles; ++qt) {
+        const int32_t cost = moba_qtile_cost(m, q_tokens, qt);
+        if (!runs.empty() && runs.back().cost == cost && runs.back().start + runs.back().count == qt)
+            runs.back().count++;
+        else
+            runs.push_back({qt, 1, cost});
+    }
+    p.n_groups = 0;
+    if ((int)runs.size() > wmk::kMaxGroups) return;
+    std::stable_sort(runs.begin(), runs.end(), [](const Run& a, const Run& b) { return a.cost > b.cost; });
+    for (size_t i = 0; i < runs.size(); ++i) {
+        p.grp_start[i] = runs[i].start;
+        p.grp_count[i] = runs[i].count;
+    }
+    p.n_groups = (int32_t)runs.size();
+}
+
+wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, bool moba, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
+    hipError_t e;
+    if (dtype == WMK_F32) {
+        if (dry_run_path() != nullptr) {
+            dry_log("attn dtype=f32 q=%d heads=%d d=%d kv=%d moba=%d\n", call.q_tokens, call.heads, call.head_dim,
+                    call.kv_total, call.moba.enabled);
+            return ok();
+        }
+        e = wmk::launch_attn_f32(call, stream);
+    } else {
+        wmk::AttnPlan p;
+        memset(&p, 0, sizeof p);
+        p.n_qtiles = (call.q_tokens + kBQ - 1) / kBQ;
+        p.n_units = p.n_qtiles * call.heads;
+        p.splits = 1;
+        if (moba) {
+            plan_moba_groups(p, call.moba, call.q_tokens);
+            p.xcd_remap = 0;
+        } else {
+            p.xcd_remap = 1;
+            plan_split(p, call.head_dim, (call.kv_total + kBK - 1) / kBK, ws, ws_bytes);
+        }
+        if (dry_run_path() != nullptr) {
+            dry_log("attn dtype=bf16 q=%d heads=%d d=%d kv=%d moba=%d units=%d qtiles=%d groups=%d split_units=%d "
+                    "splits=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total, call.moba.enabled,
+                    p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
+            for (int g = 0; g < p.n_groups; ++g) dry_log("group %d %d\n", p.grp_start[g], p.grp_count[g]);
+            return ok();
+        }
+        e = wmk::launch_attn_bf16(call, p, stream);
+    }
+    if (e != hipSuccess) return fail(WMK_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+#pragma GCC visibility push(default)
+extern "C" {
+
+size_t wmk_cache_bytes(const wmk_cache_desc* d) {
+    if (check_desc(d) != WMK_OK) return 0;
+    return (size_t)d->num_layers * (size_t)(d->sink_frames + d->window_frames) * (size_t)d->tokens_per_frame *
+           (size_t)d->num_heads * (size_t)d->head_dim * elem_size(d->dtype);
+}
+
+wmk_status wmk_cache_init(const wmk_cache_desc* d, void* k_dev, void* v_dev, size_t capacity_bytes,
+                          wmk_cache** out) {
+    wmk_status s = check_desc(d);
+    if (s != WMK_OK) return s;
+    if (k_dev == nullptr || v_dev == nullptr || out == nullptr)
+        return fail(WMK_ERR_NULL, "k_dev, v_dev and out must not be NULL");
+    if (!aligned16(k_dev) || !aligned16(v_dev)) return fail(WMK_ERR_ALIGN, "cache buffers must be 16-byte aligned");
+    const size_t need = wmk_cache_bytes(d);
+    if (capacity_bytes < need)
+        return fail(WMK_ERR_CAPACITY, "capacity %zu bytes < %zu bytes needed per K/V buffer", capacity_bytes, need);
+    wmk_cache* c = new (std::nothrow) wmk_cache;
+    if (c == nullptr) return fail(WMK_ERR_CAPACITY, "out of host memory");
+    c->d = *d;
+    c->k = (char*)k_dev;
+    c->v = (char*)v_dev;
+    c->frame_bytes = (size_t)d->tokens_per_frame * d->num_heads * d->head_dim * elem_size(d->dtype);
+    c->layer_bytes = c->frame_bytes * (size_t)(d->sink_frames + d->window_frames);
+    c->frames.assign(d->num_layers, 0);
+    *out = c;
+    return ok();
+}
+
+void wmk_cache_destroy(wmk_cache* c) { delete c; }
+
+wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                                  int32_t n_frames, hipStream_t stream) {
+    if (c == nullptr || k_new == nullptr || v_new == nullptr)
+        return fail(WMK_ERR_NULL, "cache, k_new and v_new must not be NULL");
+    const wmk_cache_desc& d = c->d;
+    if (layer < 0 || layer >= d.num_layers)
+        return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, d.num_layers);
+    if (n_frames <= 0) return fail(WMK_ERR_SHAPE, "n_frames %d <= 0", n_frames);
+    if ((int64_t)n_frames * d.tokens_per_frame > INT32_MAX)
+        return fail(WMK_ERR_SHAPE, "n_frames * tokens_per_frame exceeds 2^31 - 1");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(WMK_ERR_ALIGN, "k_new/v_new must be 16-byte aligned");
+
+    // Frames still resident after this call: sinks and the last W non-sink
+    // frames; the others would be overwritten by this same call and are skipped.
+    const int64_t F = c->frames[layer];
+    const int64_t keep_from = F + n_frames - d.window_frames;
+    wmk::CopyRange r[wmk::kMaxCopy];
+    int nr = 0;
+    int64_t run_f = -1, run_slot = -1, run_len = 0;
+    bool too_many = false;
+    auto flush = [&]() {
+        if (run_len == 0) return;
+        if (nr + 2 > wmk::kMaxCopy) {
+            too_many = true;
+            return;
+        }
+        const size_t src_off = (size_t)(run_f - F) * c->frame_bytes;
+        const size_t dst_off = (size_t)layer * c->layer_bytes + (size_t)run_slot * c->frame_bytes;
+        const int64_t bytes = run_len * (int64_t)c->frame_bytes;
+        r[nr++] = {(const char*)k_new + src_off, c->k + dst_off, bytes};
+        r[nr++] = {(const char*)v_new + src_off, c->v + dst_off, bytes};
+        run_len = 0;
+    };
+    for (int64_t f = F; f < F + n_frames; ++f) {
+        if (!(f < d.sink_frames || f >= keep_from)) continue;
+        const int64_t s = slot_of(d, f);
+        if (run_len > 0 && f == run_f + run_len && s == run_slot + run_len) {
+            ++run_len;
+        } else {
+            flush();
+            run_f = f;
+            run_slot = s;
+            run_len = 1;
+        }
+    }
+    flush();  // at most 3 runs (sinks, window up to the ring end, wrapped window)
+    if (too_many) return fail(WMK_ERR_SHAPE, "append maps to more slot ranges than one launch copies");
+    if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
+    if (dry_run_path() != nullptr) {
+        dry_log("append layer=%d F=%lld n=%d ranges=%d", layer, (long long)F, n_frames, nr / 2);
+        for (int i = 0; i < nr; i += 2)
+            dry_log(" %lld:%lld:%lld", (long long)((const char*)r[i].src - (const char*)k_new),
+                    (long long)((char*)r[i].dst - c->k), (long long)r[i].bytes);
+        dry_log("\n");
+        c->frames[layer] = F + n_frames;
+        return ok();
+    }
+    const hipError_t e = wmk::launch_copy_ranges(r, nr, stream);
+    if (e != hipSuccess) return fail(WMK_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+    c->frames[layer] = F + n_frames;
+    return ok();
+}
+
+wmk_status wmk_cache_slots(const wmk_cache* c, int32_t layer, int64_t* frame_of_slot, int64_t* frames_appended) {
+    if (c == nullptr) return fail(WMK_ERR_NULL, "cache is NULL");
+    const wmk_cache_desc& d = c->d;
+    if (layer < 0 || layer >= d.num_layers)
+        return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, d.num_layers);
+    const int64_t F = c->frames[layer];
+    if (frames_appended) *frames_appended = F;
+    if (frame_of_slot) {
+        const int n = d.sink_frames + d.window_frames;
+        for (int i = 0; i < n; ++i) frame_of_slot[i] = -1;
+        for (int64_t f = 0; f < std::min<int64_t>(F, d.sink_frames); ++f) frame_of_slot[f] = f;
+        for (int64_t f = std::max<int64_t>(d.sink_frames, F - d.window_frames); f < F; ++f)
+            frame_of_slot[slot_of(d, f)] = f;
+    }
+    return ok();
+}
+
+size_t wmk_attention_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens) {
+    if (check_head(hd) != WMK_OK || q_tokens <= 0 || hd->dtype != WMK_BF16) return 0;
+    const DeviceInfo di = device_info();
+    const int slots = di.cus * (hd->head_dim == 64 ? di.bpc64 : di.bpc128);
+    const int64_t units = (int64_t)((q_tokens + kBQ - 1) / kBQ) * hd->num_heads;
+    const int32_t tail = (int32_t)std::min<int64_t>(units, slots);
+    // pieces never exceed the number of resident workgroups
+    return wmk::attn_bf16_split_ws_bytes(hd->head_dim, tail, std::max(1, slots / std::max(1, tail)));
+}
+
+wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
+                               int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    wmk_status s = check_head(hd);
+    if (s != WMK_OK) return s;
+    if (q == nullptr || out == nullptr) return fail(WMK_ERR_NULL, "q and out must not be NULL");
+    if (n_seg < 0 || n_seg > wmk::kMaxSeg - 1) return fail(WMK_ERR_SHAPE, "n_seg %d outside [0, 4]", n_seg);
+    if (n_seg > 0 && seg == nullptr) return fail(WMK_ERR_NULL, "seg is NULL with n_seg %d", n_seg);
+    if (q_tokens <= 0) return fail(WMK_ERR_SHAPE, "q_tokens %d <= 0", q_tokens);
+    if ((s = check_scale(scale)) != WMK_OK) return s;
+    if (!aligned16(q) || !aligned16(out)) return fail(WMK_ERR_ALIGN, "q/out must be 16-byte aligned");
+    if (c != nullptr) {
+        if (layer < 0 || layer >= c->d.num_layers)
+            return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, c->d.num_layers);
+        if (c->d.num_heads != hd->num_heads || c->d.head_dim != hd->head_dim)
+            return fail(WMK_ERR_SHAPE, "head descriptor (%d x %d) does not match the cache (%d x %d)",
+                        hd->num_heads, hd->head_dim, c->d.num_heads, c->d.head_dim);
+        if (c->d.dtype != hd->dtype) return fail(WMK_ERR_DTYPE, "dtype differs from the cache's");
+    }
+    wmk::AttnCall call;
+    memset(&call, 0, sizeof call);
+    int64_t total = 0;
+    int n = 0;
+    if (c != nullptr) {
+        const int64_t valid = valid_of(c->d, c->frames[layer]);
+        if (valid > 0) {
+            const size_t base = (size_t)layer * c->layer_bytes;
+            call.kv.k[n] = c->k + base;
+            call.kv.v[n] = c->v + base;
+            total += valid * c->d.tokens_per_frame;
+            call.kv.end[n] = (int32_t)total;
+            ++n;
+        }
+    }
+    for (int i = 0; i < n_seg; ++i) {
+        if (seg[i].k == nullptr || seg[i].v == nullptr) return fail(WMK_ERR_NULL, "segment %d has a NULL k/v", i);
+        if (seg[i].tokens <= 0) return fail(WMK_ERR_SHAPE, "segment %d has %d tokens", i, seg[i].tokens);
+        if (!aligned16(seg[i].k) || !aligned16(seg[i].v))
+            return fail(WMK_ERR_ALIGN, "segment %d k/v must be 16-byte aligned", i);
+        total += seg[i].tokens;
+        if (total > INT32_MAX) return fail(WMK_ERR_SHAPE, "more than 2^31 - 1 keys");
+        call.kv.k[n] = seg[i].k;
+        call.kv.v[n] = seg[i].v;
+        call.kv.end[n] = (int32_t)total;
+        ++n;
+    }
+    call.kv.n = n;
+    call.q = q;
+    call.out = out;
+    call.q_tokens = q_tokens;
+    call.heads = hd->num_heads;
+    call.head_dim = hd->head_dim;
+    call.kv_total = (int32_t)total;
+    call.scale = scale;
+    call.moba.enabled = 0;
+    return run_attention(call, hd->dtype, false, workspace, workspace_bytes, stream);
+}
+
+wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
+                              const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    if (m == nullptr) return fail(WMK_ERR_NULL, "MoBA descriptor is NULL");
+    wmk_status s = check_head(hd);
+    if (s != WMK_OK) return s;
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return fail(WMK_ERR_NULL, "q, k, v and out must not be NULL");
+    if (m->tokens_per_frame < 1 || m->frames < 1 || m->chunk_frames < 1)
+        return fail(WMK_ERR_SHAPE, "MoBA descriptor has a non-positive field");
+    if (m->bidir_block != 0 && m->bidir_block != 1) return fail(WMK_ERR_SHAPE, "bidir_block %d not 0 or 1", m->bidir_block);
+    const int64_t L = (int64_t)m->frames * m->tokens_per_frame;
+    const int64_t total = (2 + m->bidir_block) * L;
+    if (total > INT32_MAX) return fail(WMK_ERR_SHAPE, "sequence of %lld tokens exceeds 2^31 - 1", (long long)total);
+    if ((s = check_scale(scale)) != WMK_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(WMK_ERR_ALIGN, "q/k/v/out must be 16-byte aligned");
+    wmk::AttnCall call;
+    memset(&call, 0, sizeof call);
+    call.kv.k[0] = k;
+    call.kv.v[0] = v;
+    call.kv.end[0] = (int32_t)total;
+    call.kv.n = 1;
+    call.q = q;
+    call.out = out;
+    call.q_tokens = (int32_t)total;
+    call.heads = hd->num_heads;
+    call.head_dim = hd->head_dim;
+    call.kv_total = (int32_t)total;
+    call.scale = scale;
+    call.moba.enabled = 1;
+    call.moba.part_len = (int32_t)L;
+    call.moba.chunk_len = std::min(m->chunk_frames, m->frames) * m->tokens_per_frame;
+    call.moba.parts = 2 + m->bidir_block;
+    (void)workspace;
+    (void)workspace_bytes;
+    return run_attention(call, hd->dtype, true, nullptr, 0, stream);
+}
+
+const char* wmk_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"
+#pragma GCC visibility pop

@@ -1,0 +1,81 @@
+// Internal interface between the C ABI (wmk_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace wmk {
+
+constexpr int kMaxSeg = 5;        // cache prefix + up to 4 caller segments
+constexpr int kMaxGroups = 64;    // q-tile groups of a longest-first launch order
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Keys/values seen by one attention call: the virtual concatenation of up to
+// kMaxSeg spans, each [tokens][heads][head_dim].  seg_end is the exclusive
+// prefix sum of the span lengths.
+struct KvSpans {
+    const void* k[kMaxSeg];
+    const void* v[kMaxSeg];
+    int32_t end[kMaxSeg];
+    int32_t n;
+};
+
+// The MoBA sequence [clean | noisy | block]; parts = 2 or 3.
+struct MobaShape {
+    int32_t enabled;
+    int32_t part_len;   // frames * tokens_per_frame
+    int32_t chunk_len;  // chunk_frames * tokens_per_frame
+    int32_t parts;
+};
+
+struct AttnCall {
+    const void* q;
+    void* out;
+    int32_t q_tokens;
+    int32_t heads;
+    int32_t head_dim;
+    int32_t kv_total;
+    float scale;
+    KvSpans kv;
+    MobaShape moba;
+};
+
+// Work plan for the bf16 MFMA kernel: which (head, q-tile) units run in which
+// launch order, and how the last partial round is split over the key range.
+struct AttnPlan {
+    int32_t n_qtiles;       // ceil(q_tokens / 128)
+    int32_t n_units;        // n_qtiles * heads
+    int32_t n_groups;       // > 0: q-tiles visited in this group order (longest first)
+    int32_t grp_start[kMaxGroups];
+    int32_t grp_count[kMaxGroups];
+    int32_t xcd_remap;      // 1: keep consecutive units of one head on one XCD
+    // split tail: the last `split_units` units (in launch order) run as
+    // `splits` pieces each over disjoint key-tile ranges, merged in-kernel.
+    int32_t split_units;
+    int32_t splits;
+    void* ws;               // workspace for the split tail (may be NULL when split_units == 0)
+};
+
+// bf16 MFMA attention.  Returns the launch status.
+hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t s);
+
+// Number of resident workgroups of the bf16 kernel per CU (occupancy) for head_dim.
+int attn_bf16_blocks_per_cu(int head_dim);
+
+// Workspace bytes the bf16 kernel's split tail needs for `pieces` pieces.
+size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t splits);
+
+// fp32 attention (plain SIMT; correctness path for fp32 inputs).
+hipError_t launch_attn_f32(const AttnCall& c, hipStream_t s);
+
+// Copy of up to 8 byte ranges (all multiples of 16 bytes, 16-byte aligned) in one launch.
+struct CopyRange {
+    const void* src;
+    void* dst;
+    int64_t bytes;
+};
+constexpr int kMaxCopy = 8;
+hipError_t launch_copy_ranges(const CopyRange* r, int n, hipStream_t s);
+
+}  // namespace wmk
