@@ -40,6 +40,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -50,6 +51,7 @@ constexpr int BQ = 128;  // query rows per workgroup
 constexpr int BK = 64;   // keys per tile
 constexpr int NT = 256;  // threads per workgroup (4 waves)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units (weights stay <= 256)
 
 template <int D>
 struct Cfg {
@@ -72,65 +74,87 @@ struct Params {
 
 // The tile ranges a workgroup visits: union over its rows of their allowed key
 // ranges, rounded out to whole tiles, sorted and merged (at most 4 ranges).
+// Written with fixed slots, a sorting network and selects -- no dynamically
+// indexed arrays -- so that it stays in scalar registers: an array here would
+// live in scratch memory, and every scratch read in the tile loop would wait
+// for the in-flight prefetch of the next tile.
 struct TileRanges {
-    int32_t b[4], e[4];
-    int32_t n, total;
+    int32_t b0, e0, b1, e1, b2, e2, b3, e3;
+    int32_t total;
 };
 
-__device__ __forceinline__ void add_range(int32_t* lo, int32_t* hi, int& n, int32_t a, int32_t b) {
-    if (b > a) { lo[n] = a; hi[n] = b; ++n; }
+constexpr int32_t kNone = 0x7fffffff;  // empty slot
+
+__device__ __forceinline__ void set_tiles(int32_t& l, int32_t& h, int32_t a, int32_t b) {
+    if (b > a) { l = a / BK; h = (b + BK - 1) / BK; }
 }
 
-__device__ TileRanges tile_ranges(const AttnCall& c, int32_t r0, int32_t r1) {
-    int32_t lo[4], hi[4];
-    int n = 0;
+__device__ __forceinline__ void order(int32_t& al, int32_t& ah, int32_t& bl, int32_t& bh) {
+    const bool sw = bl < al;
+    const int32_t tl = sw ? bl : al, th = sw ? bh : ah;
+    bl = sw ? al : bl;
+    bh = sw ? ah : bh;
+    al = tl;
+    ah = th;
+}
+
+__device__ __forceinline__ void emit(TileRanges& r, int k, int32_t b, int32_t e) {
+    r.b0 = k == 0 ? b : r.b0; r.e0 = k == 0 ? e : r.e0;
+    r.b1 = k == 1 ? b : r.b1; r.e1 = k == 1 ? e : r.e1;
+    r.b2 = k == 2 ? b : r.b2; r.e2 = k == 2 ? e : r.e2;
+    r.b3 = k == 3 ? b : r.b3; r.e3 = k == 3 ? e : r.e3;
+}
+
+__device__ __forceinline__ TileRanges tile_ranges(const AttnCall& c, int32_t r0, int32_t r1) {
+    int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
     if (!c.moba.enabled) {
-        add_range(lo, hi, n, 0, c.kv_total);
+        set_tiles(l0, h0, 0, c.kv_total);
     } else {
         const int32_t L = c.moba.part_len, cl = c.moba.chunk_len;
-        for (int32_t part = r0 / L; part <= (r1 - 1) / L && part < c.moba.parts; ++part) {
-            const int32_t fa = max(r0, part * L) - part * L;          // first row inside the part
-            const int32_t fb = min(r1, (part + 1) * L) - part * L - 1;  // last row inside the part
+        const int32_t pa = r0 / L, pb = min((r1 - 1) / L, c.moba.parts - 1);
+        if (pa <= 0 && 0 <= pb) {  // clean rows: block-causal prefix
+            const int32_t fb = min(r1, L) - 1;
+            set_tiles(l0, h0, 0, min((fb / cl + 1) * cl, L));
+        }
+        if (pa <= 1 && 1 <= pb) {  // noisy rows: earlier clean chunks, own noisy chunk
+            const int32_t fa = max(r0, L) - L, fb = min(r1, 2 * L) - L - 1;
             const int32_t ka = fa / cl, kb = fb / cl;
-            if (part == 0) {
-                add_range(lo, hi, n, 0, min((kb + 1) * cl, L));
-            } else if (part == 1) {
-                add_range(lo, hi, n, 0, kb * cl);
-                add_range(lo, hi, n, L + ka * cl, L + min((kb + 1) * cl, L));
-            } else {
-                add_range(lo, hi, n, 2 * L, 3 * L);
-            }
+            set_tiles(l1, h1, 0, kb * cl);
+            set_tiles(l2, h2, L + ka * cl, L + min((kb + 1) * cl, L));
         }
+        if (pa <= 2 && 2 <= pb) set_tiles(l3, h3, 2 * L, 3 * L);  // the bidirectional block
     }
-    // to tiles, then insertion sort by begin and merge overlaps
-    for (int i = 0; i < n; ++i) { lo[i] = lo[i] / BK; hi[i] = (hi[i] + BK - 1) / BK; }
-    for (int i = 1; i < n; ++i)
-        for (int j = i; j > 0 && lo[j] < lo[j - 1]; --j) {
-            int32_t t = lo[j]; lo[j] = lo[j - 1]; lo[j - 1] = t;
-            t = hi[j]; hi[j] = hi[j - 1]; hi[j - 1] = t;
-        }
-    TileRanges r;
-    r.n = 0;
-    r.total = 0;
-    for (int i = 0; i < n; ++i) {
-        if (r.n > 0 && lo[i] <= r.e[r.n - 1]) {
-            r.e[r.n - 1] = max(r.e[r.n - 1], hi[i]);
-        } else {
-            r.b[r.n] = lo[i];
-            r.e[r.n] = hi[i];
-            ++r.n;
-        }
+    order(l0, h0, l1, h1);
+    order(l2, h2, l3, h3);
+    order(l0, h0, l2, h2);
+    order(l1, h1, l3, h3);
+    order(l1, h1, l2, h2);
+    TileRanges r = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    int k = 0;
+    int32_t cb = l0, ce = h0;
+#define WMK_MERGE(L_, H_)                                      \
+    if (L_ != kNone) {                                         \
+        if (L_ <= ce) {                                        \
+            ce = max(ce, H_);                                  \
+        } else {                                               \
+            emit(r, k, cb, ce);                                \
+            ++k;                                               \
+            cb = L_;                                           \
+            ce = H_;                                           \
+        }                                                      \
     }
-    for (int i = 0; i < r.n; ++i) r.total += r.e[i] - r.b[i];
+    WMK_MERGE(l1, h1)
+    WMK_MERGE(l2, h2)
+    WMK_MERGE(l3, h3)
+#undef WMK_MERGE
+    if (cb != kNone) emit(r, k, cb, ce);
+    r.total = (r.e0 - r.b0) + (r.e1 - r.b1) + (r.e2 - r.b2) + (r.e3 - r.b3);
     return r;
 }
 
 __device__ __forceinline__ int32_t tile_at(const TileRanges& r, int32_t it) {
-    int32_t t = r.b[0] + it;
-    int32_t acc = r.e[0] - r.b[0];
-    for (int i = 1; i < 4; ++i)
-        if (i < r.n && it >= acc) { t = r.b[i] + (it - acc); acc += r.e[i] - r.b[i]; }
-    return t;
+    const int32_t n0 = r.e0 - r.b0, n1 = n0 + (r.e1 - r.b1), n2 = n1 + (r.e2 - r.b2);
+    return it < n0 ? r.b0 + it : it < n1 ? r.b1 + (it - n0) : it < n2 ? r.b2 + (it - n1) : r.b3 + (it - n2);
 }
 
 // Allowed key ranges of one query row (see wmk.h).
@@ -171,60 +195,76 @@ struct TileRegs {
     u32x4 v[4];
 };
 
-// Global -> registers for key tile `tile` (zeros past kv_total).
+// Per-lane byte offsets of this thread's K and V chunks inside a tile, relative
+// to the tile's first key row; constant over the key loop.
 template <int D>
-__device__ __forceinline__ void load_tile(const AttnCall& c, int32_t head, int32_t tile, TileRegs<D>& r) {
+struct LaneOffsets {
+    uint32_t k[Cfg<D>::KLD];
+    uint32_t v[4];
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int32_t heads, int32_t head) {
     using C = Cfg<D>;
     const int tid = threadIdx.x;
-    const int64_t stride = (int64_t)c.heads * D;
+    const uint32_t row_bytes = (uint32_t)heads * D * 2, head_bytes = (uint32_t)head * D * 2;
+    LaneOffsets<D> o;
+#pragma unroll
+    for (int i = 0; i < C::KLD; ++i)
+        o.k[i] = (uint32_t)(tid / C::KCH + i * (NT / C::KCH)) * row_bytes + head_bytes + (tid % C::KCH) * 16;
+    const int ch = (tid / 16) % C::KCH, qd = tid % 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)(qd * 4 + i) * row_bytes + head_bytes + ch * 16;
+    return o;
+}
+
+// Global -> registers for key tile `tile`.  Common case: the whole tile lies in
+// one span, so every load is a uniform base plus this lane's constant offset.
+// A tile that crosses a span end or the last key takes the per-lane path
+// (span lookup, zeros past the last key).
+template <int D>
+__device__ __forceinline__ void load_tile(const AttnCall& c, int32_t head, int32_t tile, const LaneOffsets<D>& lo,
+                                          TileRegs<D>& r) {
+    using C = Cfg<D>;
+    const int tid = threadIdx.x;
+    const int64_t row_bytes = (int64_t)c.heads * D * 2;
     const int32_t j0 = tile * BK;
     int32_t s0start;
     const int s0 = span_of(c.kv, j0, s0start);
-    const bool uniform = (j0 + BK <= c.kv.end[s0]);  // whole tile inside one span
-    // K: thread owns chunk (tid % KCH) of rows tid / KCH + i * (NT / KCH)
+    if (j0 + BK <= c.kv.end[s0]) {
+        const char* kb = (const char*)c.kv.k[s0] + (int64_t)(j0 - s0start) * row_bytes;
+        const char* vb = (const char*)c.kv.v[s0] + (int64_t)(j0 - s0start) * row_bytes;
+#pragma unroll
+        for (int i = 0; i < C::KLD; ++i) r.k[i] = *(const u32x4*)(kb + lo.k[i]);
+        if (tid < C::VIT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r.v[i] = *(const u32x4*)(vb + lo.v[i]);
+        }
+        return;
+    }
+    const int64_t stride = (int64_t)c.heads * D;
     {
         const int ch = tid % C::KCH;
 #pragma unroll
         for (int i = 0; i < C::KLD; ++i) {
             const int32_t j = j0 + tid / C::KCH + i * (NT / C::KCH);
-            const __bf16* base;
-            int64_t off;
-            if (uniform) {
-                base = (const __bf16*)c.kv.k[s0];
-                off = (int64_t)(j - s0start) * stride;
-            } else {
-                int32_t st;
-                const int s = span_of(c.kv, j, st);
-                base = (const __bf16*)c.kv.k[s];
-                off = (int64_t)(j - st) * stride;
-            }
-            if (j < c.kv_total)
-                r.k[i] = *(const u32x4*)(base + off + (int64_t)head * D + ch * 8);
-            else
-                r.k[i] = u32x4{0u, 0u, 0u, 0u};
+            int32_t st;
+            const int s = span_of(c.kv, j, st);
+            const __bf16* base = (const __bf16*)c.kv.k[s];
+            r.k[i] = u32x4{0u, 0u, 0u, 0u};
+            if (j < c.kv_total) r.k[i] = *(const u32x4*)(base + (int64_t)(j - st) * stride + (int64_t)head * D + ch * 8);
         }
     }
-    // V: item tid = (d-chunk tid / 16, key quad tid % 16), keys 4*quad .. 4*quad+3
     if (tid < C::VIT) {
         const int ch = tid / 16, qd = tid % 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int32_t j = j0 + qd * 4 + i;
-            const __bf16* base;
-            int64_t off;
-            if (uniform) {
-                base = (const __bf16*)c.kv.v[s0];
-                off = (int64_t)(j - s0start) * stride;
-            } else {
-                int32_t st;
-                const int s = span_of(c.kv, j, st);
-                base = (const __bf16*)c.kv.v[s];
-                off = (int64_t)(j - st) * stride;
-            }
-            if (j < c.kv_total)
-                r.v[i] = *(const u32x4*)(base + off + (int64_t)head * D + ch * 8);
-            else
-                r.v[i] = u32x4{0u, 0u, 0u, 0u};
+            int32_t st;
+            const int s = span_of(c.kv, j, st);
+            const __bf16* base = (const __bf16*)c.kv.v[s];
+            r.v[i] = u32x4{0u, 0u, 0u, 0u};
+            if (j < c.kv_total) r.v[i] = *(const u32x4*)(base + (int64_t)(j - st) * stride + (int64_t)head * D + ch * 8);
         }
     }
 }
@@ -256,10 +296,12 @@ __device__ __forceinline__ void store_tile(__bf16* buf, const TileRegs<D>& r) {
         const int pos = vt_pos(qd);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            const uint32_t x0 = (r.v[0][w] >> sh) & 0xffffu, x1 = (r.v[1][w] >> sh) & 0xffffu;
-            const uint32_t x2 = (r.v[2][w] >> sh) & 0xffffu, x3 = (r.v[3][w] >> sh) & 0xffffu;
-            *(u32x2*)(Vt + (ch * 8 + e) * C::VS + pos) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+            // element e of keys 0..3: low (e even) or high (e odd) half of dword e/2
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const int w = e >> 1;
+            const uint32_t lo01 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
+            const uint32_t lo23 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
+            *(u32x2*)(Vt + (ch * 8 + e) * C::VS + pos) = u32x2{lo01, lo23};
         }
     }
 }
@@ -356,12 +398,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     f32x16 o[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f;
+    float m_ref = -INFINITY, l_run = 0.0f;
     const float cs = c.scale * kLog2e;
 
+    const LaneOffsets<D> loffs = lane_offsets<D>(c.heads, head);
     TileRegs<D> regs;
     if (it0 < it1) {
-        load_tile<D>(c, head, tile_at(tr, it0), regs);
+        load_tile<D>(c, head, tile_at(tr, it0), loffs, regs);
         store_tile<D>(lds, regs);
     }
     __syncthreads();
@@ -369,7 +412,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     for (int32_t it = it0; it < it1; ++it) {
         const int stage = (it - it0) & 1;
         const bool more = it + 1 < it1;
-        if (more) load_tile<D>(c, head, tile_at(tr, it + 1), regs);
+        if (more) load_tile<D>(c, head, tile_at(tr, it + 1), loffs, regs);
 
         if (wave_has_rows) {
             const __bf16* Kl = lds + stage * C::BUF;
@@ -401,22 +444,24 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
                     }
             }
 
-            // online softmax (log2 domain)
+            // online softmax (log2 domain).  m_ref is the reference the
+            // exponentials use; it moves (and O, l are rescaled) only when a
+            // row's tile max exceeds it by more than kTau, so p <= 2^kTau.
             float mx = s[0][0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m_run, mx * cs);
-            const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-            if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+            const float mt = pair_max(mx) * cs;
+            if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
+                const float m_new = fmaxf(m_ref, mt);
+                const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+                l_run *= alpha;
+                m_ref = m_new;
             }
-            l_run *= alpha;
-            m_run = m_new;
+            const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
 
             bf16x8 pf[2][2];
             float lsum = 0.0f;
@@ -426,11 +471,15 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
                 for (int t = 0; t < 2; ++t) {
                     f32x8 e;
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_ref));
-                        lsum += e[r];
-                    }
+                    for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_use));
                     pf[kb][t] = __builtin_convertvector(e, bf16x8);
+                    // row sum of the bf16 weights the PV product uses
+                    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2) {
+                        const bf16x2 pp = {pf[kb][t][2 * q2], pf[kb][t][2 * q2 + 1]};
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum, false);
+                    }
                 }
             }
             l_run += lsum;
@@ -484,7 +533,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
                 *(f32x4*)(w + (size_t)rl * D + db * 32 + 8 * g + 4 * h) =
                     f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
         if (h == 0) {
-            w[SplitWs<D>::kO + 2 * rl] = m_run;
+            w[SplitWs<D>::kO + 2 * rl] = m_ref;
             w[SplitWs<D>::kO + 2 * rl + 1] = l_tot;
         }
     }
