@@ -1,23 +1,31 @@
 // bf16 attention on the CDNA4 matrix cores (gfx950).
 //
-// One workgroup = 4 waves = 128 query rows of one head (32 rows per wave); keys
-// are visited in tiles of 64, staged in LDS (double-buffered, one barrier per
-// tile) and shared by the 4 waves.
+// One workgroup = 8 waves = 256 query rows of one head (32 rows per wave); keys
+// are visited in tiles of 64.  K and V tiles go from global memory straight
+// into LDS (global_load_lds_dwordx4, no staging registers) and are shared by
+// the 8 waves; two K and two V buffers, one barrier per tile.
 //
-// Per wave and tile:
-//   S^T[key][q] = K . Q^T        v_mfma_f32_32x32x16_bf16, K from LDS (A), Q^T
-//                                from registers (B, loaded once).  In the 32x32
-//                                accumulator layout lane l owns query l%32 and
-//                                16 of the tile's 32 keys per block; the other 16
-//                                sit in lane l^32, so a row max or sum is a
-//                                register reduction plus one permlane32 swap.
-//   online softmax in fp32       exp2 with scale*log2(e) folded into one FMA;
-//                                the accumulator is rescaled only when some row
-//                                max of the wave grew.
-//   O^T[d][q] += V^T . P^T       the S^T accumulator, rounded to bf16, is the B
-//                                operand as it stands; V^T comes from LDS, where
-//                                it is stored transposed with its keys permuted
-//                                to the accumulator's key order.
+// Per wave, iteration j (software pipelined across tiles):
+//   softmax of tile j            fp32, log2 domain: exp2 with scale*log2(e)
+//                                folded into one FMA; the reference max moves
+//                                (and O, l are rescaled) only when a row max
+//                                grows by more than kTau.
+//   S^T(j+1) = K(j+1) . Q^T      v_mfma_f32_32x32x16_bf16; K from LDS (A), Q^T
+//                                from registers (B, loaded once).  Independent of
+//                                the softmax above, so the matrix core runs it
+//                                while the VALU does the exponentials.  In the
+//                                32x32 accumulator layout lane l owns query l%32
+//                                and 16 of each 32-key block; the other 16 sit in
+//                                lane l^32 (one permlane32 swap per reduction).
+//   O^T += V(j)^T . P(j)^T       P^T is the S^T accumulator rounded to bf16, used
+//                                as the B operand as it stands; V^T comes from
+//                                the row-major V tile through ds_read_b64_tr_b16
+//                                (transposing LDS reads), addressed so that its
+//                                key order equals the accumulator's.
+//
+// LDS tiles are unpadded [key][dim] rows with 16-byte chunks XOR-swizzled per
+// row (different swizzles for K and V) so that both read patterns are free of
+// bank conflicts.
 //
 // Masks come from key intervals: every row allows at most two half-open key
 // ranges (the whole key range at a chunk step; the MoBA ranges in training).
@@ -33,6 +41,8 @@
 // Interactive World Models", "Mix the training modes").
 #include <math.h>
 
+#include <type_traits>
+
 #include "wmk_internal.h"
 
 namespace wmk {
@@ -41,31 +51,48 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BQ = 128;  // query rows per workgroup
-constexpr int BK = 64;   // keys per tile
-constexpr int NT = 256;  // threads per workgroup (4 waves)
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int NW = 8;        // waves per workgroup
+constexpr int NT = NW * 64;  // threads per workgroup
+constexpr int BQ = NW * 32;  // query rows per workgroup
+constexpr int BK = 64;       // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units (weights stay <= 256)
 
 template <int D>
 struct Cfg {
-    static constexpr int KS = D + 8;           // LDS row stride of K (bf16 elements, 16 B pad)
-    static constexpr int VS = BK + 8;          // LDS row stride of V^T
-    static constexpr int KE = BK * KS;
-    static constexpr int VE = D * VS;
-    static constexpr int BUF = KE + VE;        // one pipeline stage
-    static constexpr int DS = D / 16;          // k-steps of S = K Q^T
-    static constexpr int DB = D / 32;          // 32-row blocks of O^T
-    static constexpr int KCH = D / 8;          // 16-byte chunks per row
-    static constexpr int KLD = BK * KCH / NT;  // K chunks loaded per thread
-    static constexpr int VIT = 16 * KCH;       // V items: (4-key quad, 8-dim chunk)
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+    static constexpr int ROWB = D * 2;                  // bytes per key row
+    static constexpr int TILEB = BK * ROWB;             // bytes per K (or V) tile
+    static constexpr int LPT = TILEB / (NT * 16);       // direct loads per thread per tile
+    static constexpr int ROWS_PER_KB = 1024 / ROWB;     // key rows per 1 KB wave load
+    static constexpr int DS = D / 16;                   // k-steps of S = K Q^T
+    static constexpr int DB = D / 32;                   // 32-row blocks of O^T
+    static constexpr int PART_ROWS = BK / LPT;          // key rows per LDS object (one per direct load)
+    static constexpr int PARTB = PART_ROWS * ROWB;      // bytes per LDS object
+    static_assert(LPT >= 1 && LPT * NT * 16 == TILEB, "tile must split into whole wave loads");
+    static_assert(PART_ROWS % 32 == 0, "a 32-key block must lie inside one LDS object");
 };
+
+// 16-byte chunk swizzles (XOR with a per-row constant, so a bijection inside
+// each row).  K: 32 rows are read at once at one logical chunk -> the swizzle
+// spreads rows over all chunk positions; it depends on row % 16 only.  V: a
+// transposing read touches 8 consecutive rows x 64 bytes -> rows r and r+1..3
+// go to different 64-byte bank groups; it depends on row % 8 only.  Because of
+// that, the per-lane part of every LDS address is fixed and all the rest
+// (k-step, key block, buffer) is a compile-time offset.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return row & 15 & (Cfg<D>::CPR - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return (((row & 3) << 2) | ((row >> 2) & 1)) & (Cfg<D>::CPR - 1); }
 
 struct Params {
     AttnCall c;
@@ -75,9 +102,8 @@ struct Params {
 // The tile ranges a workgroup visits: union over its rows of their allowed key
 // ranges, rounded out to whole tiles, sorted and merged (at most 4 ranges).
 // Written with fixed slots, a sorting network and selects -- no dynamically
-// indexed arrays -- so that it stays in scalar registers: an array here would
-// live in scratch memory, and every scratch read in the tile loop would wait
-// for the in-flight prefetch of the next tile.
+// indexed arrays -- so that it stays in scalar registers (an array would live
+// in scratch memory, whose reads wait for the in-flight tile loads).
 struct TileRanges {
     int32_t b0, e0, b1, e1, b2, e2, b3, e3;
     int32_t total;
@@ -132,16 +158,16 @@ __device__ __forceinline__ TileRanges tile_ranges(const AttnCall& c, int32_t r0,
     TileRanges r = {0, 0, 0, 0, 0, 0, 0, 0, 0};
     int k = 0;
     int32_t cb = l0, ce = h0;
-#define WMK_MERGE(L_, H_)                                      \
-    if (L_ != kNone) {                                         \
-        if (L_ <= ce) {                                        \
-            ce = max(ce, H_);                                  \
-        } else {                                               \
-            emit(r, k, cb, ce);                                \
-            ++k;                                               \
-            cb = L_;                                           \
-            ce = H_;                                           \
-        }                                                      \
+#define WMK_MERGE(L_, H_)              \
+    if (L_ != kNone) {                 \
+        if (L_ <= ce) {                \
+            ce = max(ce, H_);          \
+        } else {                       \
+            emit(r, k, cb, ce);        \
+            ++k;                       \
+            cb = L_;                   \
+            ce = H_;                   \
+        }                              \
     }
     WMK_MERGE(l1, h1)
     WMK_MERGE(l2, h2)
@@ -179,7 +205,7 @@ __device__ __forceinline__ uint32_t in_range(int32_t j, int32_t lo, int32_t hi) 
     return (uint32_t)(j - lo) < (uint32_t)(hi - lo) ? 1u : 0u;
 }
 
-// Element offset of key j (head `head`) inside its span, and the span index.
+// Span holding key j, and the span's first key.
 __device__ __forceinline__ int span_of(const KvSpans& kv, int32_t j, int32_t& start) {
     int s = 0;
     start = 0;
@@ -189,120 +215,101 @@ __device__ __forceinline__ int span_of(const KvSpans& kv, int32_t j, int32_t& st
     return s;
 }
 
+// This thread's share of the direct tile loads: for each of its LPT wave loads
+// of a K (or V) tile, the key row inside the tile it fills and the byte offset
+// of the (swizzle-mapped) source chunk inside that key row's head slice.
 template <int D>
-struct TileRegs {
-    u32x4 k[Cfg<D>::KLD];
-    u32x4 v[4];
-};
-
-// Per-lane byte offsets of this thread's K and V chunks inside a tile, relative
-// to the tile's first key row; constant over the key loop.
-template <int D>
-struct LaneOffsets {
-    uint32_t k[Cfg<D>::KLD];
-    uint32_t v[4];
+struct LoadMap {
+    int32_t row[Cfg<D>::LPT];
+    uint32_t koff[Cfg<D>::LPT];
+    uint32_t voff[Cfg<D>::LPT];
 };
 
 template <int D>
-__device__ __forceinline__ LaneOffsets<D> lane_offsets(int32_t heads, int32_t head) {
+__device__ __forceinline__ LoadMap<D> load_map() {
     using C = Cfg<D>;
-    const int tid = threadIdx.x;
-    const uint32_t row_bytes = (uint32_t)heads * D * 2, head_bytes = (uint32_t)head * D * 2;
-    LaneOffsets<D> o;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    LoadMap<D> m;
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i)
-        o.k[i] = (uint32_t)(tid / C::KCH + i * (NT / C::KCH)) * row_bytes + head_bytes + (tid % C::KCH) * 16;
-    const int ch = (tid / 16) % C::KCH, qd = tid % 16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o.v[i] = (uint32_t)(qd * 4 + i) * row_bytes + head_bytes + ch * 16;
-    return o;
+    for (int i = 0; i < C::LPT; ++i) {
+        // load i of every wave fills LDS object (part) i; wave w fills its 1 KB block w
+        const int row = i * C::PART_ROWS + wave * C::ROWS_PER_KB + lane / C::CPR;  // key row in the tile
+        const int phys = lane % C::CPR;                                           // chunk position it lands in
+        m.row[i] = row;
+        m.koff[i] = (uint32_t)((phys ^ swz_k<D>(row)) * 16);
+        m.voff[i] = (uint32_t)((phys ^ swz_v<D>(row)) * 16);
+    }
+    return m;
 }
 
-// Global -> registers for key tile `tile`.  Common case: the whole tile lies in
-// one span, so every load is a uniform base plus this lane's constant offset.
-// A tile that crosses a span end or the last key takes the per-lane path
-// (span lookup, zeros past the last key).
+// The LDS objects of one K or V buffer: part i holds key rows
+// [i * PART_ROWS, (i + 1) * PART_ROWS), each unpadded [row][dim].
 template <int D>
-__device__ __forceinline__ void load_tile(const AttnCall& c, int32_t head, int32_t tile, const LaneOffsets<D>& lo,
-                                          TileRegs<D>& r) {
+struct Buf {
+    char LDS_AS* part[Cfg<D>::LPT];
+    // row kb * 32 + r (0 <= r < 32) of the tile: the object is known at compile
+    // time from kb, so the compiler can keep the objects apart
+    template <int KB>
+    __device__ __forceinline__ char LDS_AS* block_row(int r) const {
+        constexpr int P = (KB * 32) / Cfg<D>::PART_ROWS, R0 = (KB * 32) % Cfg<D>::PART_ROWS;
+        return part[P] + (R0 + r) * Cfg<D>::ROWB;
+    }
+};
+
+// Issue the direct loads of key tile `tile` into LDS (kbuf and/or vbuf).
+// Common case: the tile lies inside one span -> uniform base + per-lane
+// offsets.  A tile crossing a span end or the last key looks up each row's
+// span; rows past the last key read the last key instead (finite data that
+// the mask drops).
+template <int D>
+__device__ __forceinline__ void issue_tile(const AttnCall& c, int32_t head, int32_t tile, const LoadMap<D>& m,
+                                           const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
     using C = Cfg<D>;
-    const int tid = threadIdx.x;
+    const int wave = threadIdx.x >> 6;
     const int64_t row_bytes = (int64_t)c.heads * D * 2;
+    const int64_t head_off = (int64_t)head * D * 2;
     const int32_t j0 = tile * BK;
     int32_t s0start;
     const int s0 = span_of(c.kv, j0, s0start);
     if (j0 + BK <= c.kv.end[s0]) {
-        const char* kb = (const char*)c.kv.k[s0] + (int64_t)(j0 - s0start) * row_bytes;
-        const char* vb = (const char*)c.kv.v[s0] + (int64_t)(j0 - s0start) * row_bytes;
+        // whole tile inside one span: uniform base, per-lane constant offsets
+        const char* kb = (const char*)c.kv.k[s0] + ((int64_t)(j0 - s0start) * row_bytes + head_off);
+        const char* vb = (const char*)c.kv.v[s0] + ((int64_t)(j0 - s0start) * row_bytes + head_off);
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) r.k[i] = *(const u32x4*)(kb + lo.k[i]);
-        if (tid < C::VIT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) r.v[i] = *(const u32x4*)(vb + lo.v[i]);
+        for (int i = 0; i < C::LPT; ++i) {
+            const uint32_t roff = (uint32_t)m.row[i] * (uint32_t)row_bytes;
+            if (do_k)
+                __builtin_amdgcn_global_load_lds((const void*)(kb + (roff + m.koff[i])),
+                                                 (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
+            if (do_v)
+                __builtin_amdgcn_global_load_lds((const void*)(vb + (roff + m.voff[i])),
+                                                 (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
         }
         return;
     }
-    const int64_t stride = (int64_t)c.heads * D;
-    {
-        const int ch = tid % C::KCH;
+    // tile crossing a span end or the last key: per-row span (pointers picked by
+    // selects over the uniform span table); rows past the last key read the
+    // last key instead (finite data that the mask drops)
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int32_t j = j0 + tid / C::KCH + i * (NT / C::KCH);
-            int32_t st;
-            const int s = span_of(c.kv, j, st);
-            const __bf16* base = (const __bf16*)c.kv.k[s];
-            r.k[i] = u32x4{0u, 0u, 0u, 0u};
-            if (j < c.kv_total) r.k[i] = *(const u32x4*)(base + (int64_t)(j - st) * stride + (int64_t)head * D + ch * 8);
-        }
-    }
-    if (tid < C::VIT) {
-        const int ch = tid / 16, qd = tid % 16;
+    for (int i = 0; i < C::LPT; ++i) {
+        const int32_t j = min(j0 + m.row[i], c.kv_total - 1);
+        const char* kb = (const char*)c.kv.k[0];
+        const char* vb = (const char*)c.kv.v[0];
+        int32_t st = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int32_t j = j0 + qd * 4 + i;
-            int32_t st;
-            const int s = span_of(c.kv, j, st);
-            const __bf16* base = (const __bf16*)c.kv.v[s];
-            r.v[i] = u32x4{0u, 0u, 0u, 0u};
-            if (j < c.kv_total) r.v[i] = *(const u32x4*)(base + (int64_t)(j - st) * stride + (int64_t)head * D + ch * 8);
+        for (int x = 0; x < kMaxSeg - 1; ++x) {
+            const bool past = (x < c.kv.n - 1) && (j >= c.kv.end[x]);
+            kb = past ? (const char*)c.kv.k[x + 1] : kb;
+            vb = past ? (const char*)c.kv.v[x + 1] : vb;
+            st = past ? c.kv.end[x] : st;
         }
-    }
-}
-
-// Position of key quad qd inside a V^T row: within each group of 16 keys the
-// quads are stored in the order 0, 2, 1, 3, so that lanes 0-31 of the PV
-// operand read keys {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15} as one
-// contiguous 16-byte vector -- the key order of the S^T accumulator rows.
-__device__ __forceinline__ int vt_pos(int qd) {
-    return (qd >> 2) * 16 + (((qd & 1) << 1) | ((qd >> 1) & 1)) * 4;
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(__bf16* buf, const TileRegs<D>& r) {
-    using C = Cfg<D>;
-    const int tid = threadIdx.x;
-    __bf16* Kl = buf;
-    __bf16* Vt = buf + C::KE;
-    {
-        const int ch = tid % C::KCH;
-#pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int row = tid / C::KCH + i * (NT / C::KCH);
-            *(u32x4*)(Kl + row * C::KS + ch * 8) = r.k[i];
-        }
-    }
-    if (tid < C::VIT) {
-        const int ch = tid / 16, qd = tid % 16;
-        const int pos = vt_pos(qd);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // element e of keys 0..3: low (e even) or high (e odd) half of dword e/2
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const int w = e >> 1;
-            const uint32_t lo01 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
-            const uint32_t lo23 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
-            *(u32x2*)(Vt + (ch * 8 + e) * C::VS + pos) = u32x2{lo01, lo23};
-        }
+        const int64_t rel = (int64_t)(j - st) * row_bytes + head_off;
+        if (do_k)
+            __builtin_amdgcn_global_load_lds((const void*)(kb + rel + m.koff[i]),
+                                             (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
+        if (do_v)
+            __builtin_amdgcn_global_load_lds((const void*)(vb + rel + m.voff[i]),
+                                             (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
     }
 }
 
@@ -315,8 +322,68 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Per-lane LDS byte offsets (relative to an LDS object), fixed for the kernel.
+template <int D>
+struct LdsAddr {
+    uint32_t k[Cfg<D>::DS];  // A operand of S^T, k-step ds: row l32, chunk (2 ds + h) ^ swz
+    uint32_t v[Cfg<D>::DB];  // V^T fragment of O block db (t = u = 0, block 0)
+};
+
+template <int D>
+__device__ __forceinline__ LdsAddr<D> lds_addr(int lane) {
+    using C = Cfg<D>;
+    LdsAddr<D> a;
+    const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds)
+        a.k[ds] = (uint32_t)(l32 * C::ROWB + (((2 * ds + h) ^ swz_k<D>(l32)) * 16));
+    // transposing reads: in a 16-lane group, lane 4e+q names row 4h+e, dims 4q..4q+3
+    // of its 16-dim half g&1 (g = lane/16, h = g/2)
+    const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3, hh = g >> 1;
+    const int r = 4 * hh + e;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+        const int d = db * 32 + 16 * (g & 1) + 4 * q;
+        a.v[db] = (uint32_t)(r * C::ROWB + (((d >> 3) ^ swz_v<D>(r)) * 16) + (d & 7) * 2);
+    }
+    return a;
+}
+
+// S^T = K Q^T for one tile (two blocks of 32 keys), K from an LDS buffer.
+template <int D>
+__device__ __forceinline__ void qk_tile(const Buf<D>& kbuf, const bf16x8* qf, const LdsAddr<D>& la, f32x16* s) {
+    using C = Cfg<D>;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    const char LDS_AS* b0 = kbuf.template block_row<0>(0);
+    const char LDS_AS* b1 = kbuf.template block_row<1>(0);
+#pragma unroll
+    for (int ds = 0; ds < C::DS; ++ds) {
+        const bf16x8 a0 = *(const bf16x8 LDS_AS*)(b0 + la.k[ds]);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ds], s[0], 0, 0, 0);
+        const bf16x8 a1 = *(const bf16x8 LDS_AS*)(b1 + la.k[ds]);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ds], s[1], 0, 0, 0);
+    }
+}
+
+// V^T fragment (A operand) for O block db, key block KB, k-step t.  Within a
+// 16-lane group, lane 4e+q addresses key row (.. + e) at dims 4q..4q+3 of its
+// 16-dim half; the transposing read hands lane i dim (i%4) of the rows named by
+// lanes i/4, i/4+4, i/4+8, i/4+12, i.e. one dim (db*32 + lane%32) for 4 keys.
+// Two reads give the 8 keys of this lane's half: 16t + 8u + 4h + {0..3}, the
+// key order of the S^T accumulator registers 8t..8t+7.
+template <int D, int KB>
+__device__ __forceinline__ bf16x8 v_frag(const Buf<D>& vbuf, const LdsAddr<D>& la, int db, int t) {
+    using C = Cfg<D>;
+    const char LDS_AS* base = vbuf.template block_row<KB>(16 * t) + la.v[db];
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)base);
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(base + 8 * C::ROWB));
+    const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Workspace of the split tail: per split unit a counter, then per piece the
-// unnormalized O (BQ x D fp32) and per-row (max, sum).
+// unnormalized O (BQ x D fp32) and per-row (max reference, sum).
 template <int D>
 struct SplitWs {
     static constexpr size_t kO = (size_t)BQ * D;
@@ -332,7 +399,27 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     using C = Cfg<D>;
     const AttnCall& c = prm.c;
     const AttnPlan& p = prm.p;
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::BUF];
+    // Separate LDS objects, each named statically in the unrolled loop below
+    // (buffer stage x part), so the compiler can tell the objects being filled
+    // by direct loads from the ones being read -- and the direct loads of one
+    // tile from each other -- and adds no waits between them.
+    __shared__ __attribute__((aligned(1024))) char k0p0[C::PARTB];
+    __shared__ __attribute__((aligned(1024))) char k0p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char k1p0[C::PARTB];
+    __shared__ __attribute__((aligned(1024))) char k1p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char v0p0[C::PARTB];
+    __shared__ __attribute__((aligned(1024))) char v0p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char v1p0[C::PARTB];
+    __shared__ __attribute__((aligned(1024))) char v1p1[C::LPT > 1 ? C::PARTB : 16];
+    static_assert(C::LPT <= 2, "at most two LDS objects per buffer");
+    auto mkbuf = [](char* p0, char* p1) {
+        Buf<D> b;
+        b.part[0] = (char LDS_AS*)p0;
+        if constexpr (C::LPT > 1) b.part[C::LPT - 1] = (char LDS_AS*)p1;
+        return b;
+    };
+    const Buf<D> kb0 = mkbuf(k0p0, k0p1), kb1 = mkbuf(k1p0, k1p1);
+    const Buf<D> vb0 = mkbuf(v0p0, v0p1), vb1 = mkbuf(v1p0, v1p1);
     __shared__ int s_last;
 
     // ---- which unit (head, q-tile) and which key-tile range this workgroup runs
@@ -400,36 +487,36 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.0f;
     const float cs = c.scale * kLog2e;
+    const LoadMap<D> lm = load_map<D>();
+    const LdsAddr<D> la = lds_addr<D>(lane);
 
-    const LaneOffsets<D> loffs = lane_offsets<D>(c.heads, head);
-    TileRegs<D> regs;
+    // ---- prologue: K(it0), V(it0) and K(it0+1) into LDS; S^T(it0)
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
     if (it0 < it1) {
-        load_tile<D>(c, head, tile_at(tr, it0), loffs, regs);
-        store_tile<D>(lds, regs);
+        issue_tile<D>(c, head, tile_at(tr, it0), lm, kb0, vb0, true, true);
+        if (it0 + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it0 + 1), lm, kb1, vb1, true, false);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave_has_rows) qk_tile<D>(kb0, qf, la, s);
+        __syncthreads();  // K(it0) is read; the first iteration refills its buffer
     }
-    __syncthreads();
 
-    for (int32_t it = it0; it < it1; ++it) {
-        const int stage = (it - it0) & 1;
-        const bool more = it + 1 < it1;
-        if (more) load_tile<D>(c, head, tile_at(tr, it + 1), loffs, regs);
+    // One key tile; ST (compile time) is the buffer holding K(it) and V(it);
+    // K(it+1) is in the other K buffer.  Fills K(it+2) into K buffer ST and
+    // V(it+1) into the other V buffer while it computes.
+    auto step = [&](auto st_tag, int32_t it) {
+        constexpr int ST = decltype(st_tag)::value;
+        const Buf<D>& kcur = ST ? kb1 : kb0;
+        const Buf<D>& knext = ST ? kb0 : kb1;
+        const Buf<D>& vcur = ST ? vb1 : vb0;
+        const Buf<D>& vnext = ST ? vb0 : vb1;
+        if (it + 2 < it1) issue_tile<D>(c, head, tile_at(tr, it + 2), lm, kcur, vcur, true, false);
+        if (it + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it + 1), lm, knext, vnext, false, true);
 
         if (wave_has_rows) {
-            const __bf16* Kl = lds + stage * C::BUF;
-            const __bf16* Vt = Kl + C::KE;
             const int32_t j0 = tile_at(tr, it) * BK;
-
-            // S^T = K Q^T for two blocks of 32 keys
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int ds = 0; ds < C::DS; ++ds) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 a = *(const bf16x8*)(Kl + (kb * 32 + l32) * C::KS + ds * 16 + h * 8);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], s[kb], 0, 0, 0);
-                }
-            }
-
             // mask: skipped when every row of the wave allows the whole tile
             const uint32_t lane_full = (row_ok ? 0u : 1u) | ((uint32_t)(lo0 <= j0) & (uint32_t)(j0 + BK <= hi0)) |
                                        ((uint32_t)(lo1 <= j0) & (uint32_t)(j0 + BK <= hi1));
@@ -444,9 +531,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
                     }
             }
 
-            // online softmax (log2 domain).  m_ref is the reference the
-            // exponentials use; it moves (and O, l are rescaled) only when a
-            // row's tile max exceeds it by more than kTau, so p <= 2^kTau.
+            // online softmax: m_ref moves (and O, l rescale) only when a row's
+            // tile max exceeds it by more than kTau, so p <= 2^kTau
             float mx = s[0][0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
@@ -465,16 +551,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
 
             bf16x8 pf[2][2];
             float lsum = 0.0f;
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x8 e;
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_use));
+                    for (int r = 0; r < 8; ++r)
+                        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_use));
                     pf[kb][t] = __builtin_convertvector(e, bf16x8);
-                    // row sum of the bf16 weights the PV product uses
-                    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
                     for (int q2 = 0; q2 < 4; ++q2) {
                         const bf16x2 pp = {pf[kb][t][2 * q2], pf[kb][t][2 * q2 + 1]};
@@ -484,24 +570,29 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
             }
             l_run += lsum;
 
-            // O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const bf16x8 a =
-                            *(const bf16x8*)(Vt + (db * 32 + l32) * C::VS + (2 * kb + t) * 16 + h * 8);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][t], o[db], 0, 0, 0);
-                    }
-                }
-            }
-        }
+            // S^T of the next tile: independent of the exponentials above
+            if (it + 1 < it1) qk_tile<D>(knext, qf, la, s);
 
-        if (more) store_tile<D>(lds + (stage ^ 1) * C::BUF, regs);
+            // O^T += V^T P^T for this tile
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 0>(vcur, la, db, t), pf[0][t], o[db],
+                                                                    0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 1>(vcur, la, db, t), pf[1][t], o[db],
+                                                                    0, 0, 0);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    int32_t it = it0;
+    for (; it + 1 < it1; it += 2) {
+        step(std::integral_constant<int, 0>{}, it);
+        step(std::integral_constant<int, 1>{}, it + 1);
     }
+    if (it < it1) step(std::integral_constant<int, 0>{}, it);
 
     const float l_tot = pair_sum(l_run);
     __bf16* op = (__bf16*)c.out + (int64_t)row * stride + (int64_t)head * D;
@@ -593,6 +684,8 @@ __global__ void zero_ints(int* p, int n) {
 }
 
 }  // namespace
+
+int attn_bf16_block_q() { return BQ; }
 
 size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t splits) {
     if (split_units <= 0 || splits <= 0) return 0;

@@ -128,11 +128,11 @@ std::mutex g_dev_mu;
 std::vector<DeviceInfo> g_dev;
 
 DeviceInfo device_info() {
-    if (dry_run_path() != nullptr) {  // no device: an MI355X-like 256 CUs, 2 workgroups each
+    if (dry_run_path() != nullptr) {  // no device: an MI355X-like 256 CUs, one workgroup each
         DeviceInfo di;
         di.cus = 256;
-        di.bpc64 = 2;
-        di.bpc128 = 2;
+        di.bpc64 = 1;
+        di.bpc128 = 1;
         return di;
     }
     int dev = 0;
@@ -151,7 +151,7 @@ DeviceInfo device_info() {
     return di;
 }
 
-constexpr int kBQ = 128, kBK = 64;
+constexpr int kBK = 64;
 constexpr int kMinTilesPerPiece = 8;
 
 // Split the last, partly filled round of units over the whole GPU when the
@@ -176,7 +176,8 @@ void plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws
 
 // Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
 int32_t moba_qtile_cost(const wmk::MobaShape& m, int32_t q_tokens, int32_t qt) {
-    const int32_t r0 = qt * kBQ, r1 = std::min(r0 + kBQ, q_tokens);
+    const int32_t bq = wmk::attn_bf16_block_q();
+    const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, q_tokens);
     const int32_t L = m.part_len, cl = m.chunk_len;
     std::vector<std::pair<int32_t, int32_t>> iv;
     for (int32_t part = r0 / L; part <= (r1 - 1) / L && part < m.parts; ++part) {
@@ -245,7 +246,8 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, bool moba, 
     } else {
         wmk::AttnPlan p;
         memset(&p, 0, sizeof p);
-        p.n_qtiles = (call.q_tokens + kBQ - 1) / kBQ;
+        const int32_t bq = wmk::attn_bf16_block_q();
+        p.n_qtiles = (call.q_tokens + bq - 1) / bq;
         p.n_units = p.n_qtiles * call.heads;
         p.splits = 1;
         if (moba) {
@@ -256,9 +258,9 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, bool moba, 
             plan_split(p, call.head_dim, (call.kv_total + kBK - 1) / kBK, ws, ws_bytes);
         }
         if (dry_run_path() != nullptr) {
-            dry_log("attn dtype=bf16 q=%d heads=%d d=%d kv=%d moba=%d units=%d qtiles=%d groups=%d split_units=%d "
-                    "splits=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total, call.moba.enabled,
-                    p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
+            dry_log("attn dtype=bf16 q=%d heads=%d d=%d kv=%d moba=%d bq=%d units=%d qtiles=%d groups=%d "
+                    "split_units=%d splits=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total,
+                    call.moba.enabled, bq, p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
             for (int g = 0; g < p.n_groups; ++g) dry_log("group %d %d\n", p.grp_start[g], p.grp_count[g]);
             return ok();
         }
@@ -387,7 +389,8 @@ size_t wmk_attention_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens) 
     if (check_head(hd) != WMK_OK || q_tokens <= 0 || hd->dtype != WMK_BF16) return 0;
     const DeviceInfo di = device_info();
     const int slots = di.cus * (hd->head_dim == 64 ? di.bpc64 : di.bpc128);
-    const int64_t units = (int64_t)((q_tokens + kBQ - 1) / kBQ) * hd->num_heads;
+    const int32_t bq = wmk::attn_bf16_block_q();
+    const int64_t units = (int64_t)((q_tokens + bq - 1) / bq) * hd->num_heads;
     const int32_t tail = (int32_t)std::min<int64_t>(units, slots);
     // pieces never exceed the number of resident workgroups
     return wmk::attn_bf16_split_ws_bytes(hd->head_dim, tail, std::max(1, slots / std::max(1, tail)));

@@ -44,7 +44,7 @@ struct AttnCall {
 // Work plan for the bf16 MFMA kernel: which (head, q-tile) units run in which
 // launch order, and how the last partial round is split over the key range.
 struct AttnPlan {
-    int32_t n_qtiles;       // ceil(q_tokens / 128)
+    int32_t n_qtiles;       // ceil(q_tokens / attn_bf16_block_q())
     int32_t n_units;        // n_qtiles * heads
     int32_t n_groups;       // > 0: q-tiles visited in this group order (longest first)
     int32_t grp_start[kMaxGroups];
@@ -59,6 +59,9 @@ struct AttnPlan {
 
 // bf16 MFMA attention.  Returns the launch status.
 hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t s);
+
+// Query rows per workgroup (q-tile) of the bf16 kernel.
+int attn_bf16_block_q();
 
 // Number of resident workgroups of the bf16 kernel per CU (occupancy) for head_dim.
 int attn_bf16_blocks_per_cu(int head_dim);

@@ -225,7 +225,8 @@ def _last_attn(dry):
 
 def test_plan_of_the_18_slot_step(lib, dry):
     """832x464 step with a warm cache: 14 resident frames + the 4-frame chunk = 27144 keys;
-    48 q-tiles x 12 heads; with workspace the 64 units past two waves of 256 CUs are split 8 ways."""
+    q-tiles of the kernel's block size x 12 heads; with workspace, the units past the last full
+    round of 256 CUs (one workgroup each in the dry-run device model) are split over the GPU."""
     d = _desc()
     _, h = _init(lib, d)
     for _ in range(4):
@@ -233,12 +234,19 @@ def test_plan_of_the_18_slot_step(lib, dry):
     hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
     assert _attn(lib, h, 0, hd, 6032, [(QBUF, SBUF, 6032)]) == wmk.WMK_OK
     p = _last_attn(dry)
-    assert (p["kv"], p["units"], p["qtiles"], p["split_units"]) == ("27144", "576", "48", "0")
+    bq = int(p["bq"])
+    qtiles = (6032 + bq - 1) // bq
+    assert (p["kv"], p["units"], p["qtiles"], p["split_units"]) == ("27144", str(12 * qtiles), str(qtiles), "0")
     wsb = lib.wmk_attention_workspace_bytes(ctypes.byref(hd), 6032)
     assert wsb > 0
     assert _attn(lib, h, 0, hd, 6032, [(QBUF, SBUF, 6032)], ws=0x60000000, wsb=wsb) == wmk.WMK_OK
     p = _last_attn(dry)
-    assert (p["split_units"], p["splits"]) == ("64", "8")
+    tail = (12 * qtiles) % 256
+    assert int(p["split_units"]) == tail
+    assert int(p["splits"]) == min(256 // tail, (27144 + 63) // 64 // 8)
+    # too little workspace: no split
+    assert _attn(lib, h, 0, hd, 6032, [(QBUF, SBUF, 6032)], ws=0x60000000, wsb=wsb // 4) == wmk.WMK_OK
+    assert _last_attn(dry)["split_units"] == "0"
     # empty cache and no segment: planned, zero keys
     _, h2 = _init(lib, d)
     assert _attn(lib, h2, 0, hd, 100, []) == wmk.WMK_OK
@@ -247,7 +255,7 @@ def test_plan_of_the_18_slot_step(lib, dry):
     lib.wmk_cache_destroy(h2)
 
 
-def _oracle_qtile_cost(qt, tpf, frames, cf, bq=128, bk=64):
+def _oracle_qtile_cost(qt, tpf, frames, cf, bq, bk=64):
     n = 3 * frames * tpf
     tiles = set()
     for i in range(qt * bq, min((qt + 1) * bq, n)):
@@ -263,8 +271,9 @@ def test_moba_launch_order_is_longest_first(lib, dry, tpf, frames, cf):
     assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088, None, 0,
                                   None) == wmk.WMK_OK
     n = 3 * frames * tpf
-    nqt = (n + 127) // 128
     p = _last_attn(dry)
+    bq = int(p["bq"])
+    nqt = (n + bq - 1) // bq
     assert int(p["q"]) == n and int(p["qtiles"]) == nqt and int(p["groups"]) > 0
     groups = [tuple(int(x) for x in ln.split()[1:]) for ln in dry.read_text().splitlines() if ln.startswith("group")]
     groups = groups[-int(p["groups"]):]
@@ -272,7 +281,7 @@ def test_moba_launch_order_is_longest_first(lib, dry, tpf, frames, cf):
     assert sorted(order) == list(range(nqt))
     step = 1 if nqt < 200 else 7
     sample = order[::step]
-    costs = [_oracle_qtile_cost(qt, tpf, frames, cf) for qt in sample]
+    costs = [_oracle_qtile_cost(qt, tpf, frames, cf, bq) for qt in sample]
     assert all(a >= b for a, b in zip(costs, costs[1:]))
 
 
