@@ -205,30 +205,43 @@ __device__ __forceinline__ uint32_t in_range(int32_t j, int32_t lo, int32_t hi) 
     return (uint32_t)(j - lo) < (uint32_t)(hi - lo) ? 1u : 0u;
 }
 
-// Span holding key j, and the span's first key.
-__device__ __forceinline__ int span_of(const KvSpans& kv, int32_t j, int32_t& start) {
-    int s = 0;
-    start = 0;
+// Span holding key j: base pointers, first and past-the-end key.  Written with
+// static indices and selects so that, for a uniform j, it stays in scalar
+// registers (dynamic indexing would reload the kernel arguments from memory).
+struct SpanSel {
+    const char* k;
+    const char* v;
+    int32_t start, end;
+};
+
+__device__ __forceinline__ SpanSel span_sel(const KvSpans& kv, int32_t j) {
+    SpanSel r{(const char*)kv.k[0], (const char*)kv.v[0], 0, kv.end[0]};
 #pragma unroll
-    for (int x = 0; x < kMaxSeg - 1; ++x)
-        if (x < kv.n - 1 && j >= kv.end[x]) { s = x + 1; start = kv.end[x]; }
-    return s;
+    for (int x = 0; x < kMaxSeg - 1; ++x) {
+        const bool past = (x < kv.n - 1) && (j >= kv.end[x]);
+        r.k = past ? (const char*)kv.k[x + 1] : r.k;
+        r.v = past ? (const char*)kv.v[x + 1] : r.v;
+        r.start = past ? kv.end[x] : r.start;
+        r.end = past ? kv.end[x + 1] : r.end;
+    }
+    return r;
 }
 
 // This thread's share of the direct tile loads: for each of its LPT wave loads
 // of a K (or V) tile, the key row inside the tile it fills and the byte offset
-// of the (swizzle-mapped) source chunk inside that key row's head slice.
+// (from the tile's first key row of this head) of the swizzle-mapped source
+// chunk for K and for V.
 template <int D>
 struct LoadMap {
     int32_t row[Cfg<D>::LPT];
-    uint32_t koff[Cfg<D>::LPT];
-    uint32_t voff[Cfg<D>::LPT];
+    uint32_t kg[Cfg<D>::LPT];
+    uint32_t vg[Cfg<D>::LPT];
 };
 
 template <int D>
-__device__ __forceinline__ LoadMap<D> load_map() {
+__device__ __forceinline__ LoadMap<D> load_map(int wave, uint32_t row_bytes) {
     using C = Cfg<D>;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
     LoadMap<D> m;
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
@@ -236,8 +249,8 @@ __device__ __forceinline__ LoadMap<D> load_map() {
         const int row = i * C::PART_ROWS + wave * C::ROWS_PER_KB + lane / C::CPR;  // key row in the tile
         const int phys = lane % C::CPR;                                           // chunk position it lands in
         m.row[i] = row;
-        m.koff[i] = (uint32_t)((phys ^ swz_k<D>(row)) * 16);
-        m.voff[i] = (uint32_t)((phys ^ swz_v<D>(row)) * 16);
+        m.kg[i] = (uint32_t)row * row_bytes + (uint32_t)((phys ^ swz_k<D>(row)) * 16);
+        m.vg[i] = (uint32_t)row * row_bytes + (uint32_t)((phys ^ swz_v<D>(row)) * 16);
     }
     return m;
 }
@@ -263,55 +276,50 @@ struct Buf {
 // the mask drops).
 template <int D>
 __device__ __forceinline__ void issue_tile(const AttnCall& c, int32_t head, int32_t tile, const LoadMap<D>& m,
-                                           const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
+                                           int wave, const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
     using C = Cfg<D>;
-    const int wave = threadIdx.x >> 6;
     const int64_t row_bytes = (int64_t)c.heads * D * 2;
     const int64_t head_off = (int64_t)head * D * 2;
     const int32_t j0 = tile * BK;
-    int32_t s0start;
-    const int s0 = span_of(c.kv, j0, s0start);
-    if (j0 + BK <= c.kv.end[s0]) {
-        // whole tile inside one span: uniform base, per-lane constant offsets
-        const char* kb = (const char*)c.kv.k[s0] + ((int64_t)(j0 - s0start) * row_bytes + head_off);
-        const char* vb = (const char*)c.kv.v[s0] + ((int64_t)(j0 - s0start) * row_bytes + head_off);
+    const SpanSel sp = span_sel(c.kv, j0);
+    if (j0 + BK <= sp.end) {
+        // whole tile inside one span: uniform base + per-lane constant offset
+        const int64_t base = (int64_t)(j0 - sp.start) * row_bytes + head_off;
+        const char* kb = sp.k + base;
+        const char* vb = sp.v + base;
 #pragma unroll
         for (int i = 0; i < C::LPT; ++i) {
-            const uint32_t roff = (uint32_t)m.row[i] * (uint32_t)row_bytes;
             if (do_k)
-                __builtin_amdgcn_global_load_lds((const void*)(kb + (roff + m.koff[i])),
+                __builtin_amdgcn_global_load_lds((const void*)(kb + m.kg[i]),
                                                  (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
             if (do_v)
-                __builtin_amdgcn_global_load_lds((const void*)(vb + (roff + m.voff[i])),
+                __builtin_amdgcn_global_load_lds((const void*)(vb + m.vg[i]),
                                                  (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
         }
         return;
     }
-    // tile crossing a span end or the last key: per-row span (pointers picked by
-    // selects over the uniform span table); rows past the last key read the
-    // last key instead (finite data that the mask drops)
+    // tile crossing a span end or the last key: per-row span; rows past the
+    // last key read the last key instead (finite data that the mask drops)
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
         const int32_t j = min(j0 + m.row[i], c.kv_total - 1);
-        const char* kb = (const char*)c.kv.k[0];
-        const char* vb = (const char*)c.kv.v[0];
-        int32_t st = 0;
-#pragma unroll
-        for (int x = 0; x < kMaxSeg - 1; ++x) {
-            const bool past = (x < c.kv.n - 1) && (j >= c.kv.end[x]);
-            kb = past ? (const char*)c.kv.k[x + 1] : kb;
-            vb = past ? (const char*)c.kv.v[x + 1] : vb;
-            st = past ? c.kv.end[x] : st;
-        }
-        const int64_t rel = (int64_t)(j - st) * row_bytes + head_off;
+        const SpanSel r = span_sel(c.kv, j);
+        const int64_t rel = (int64_t)(j - r.start) * row_bytes + head_off - (int64_t)m.row[i] * row_bytes;
         if (do_k)
-            __builtin_amdgcn_global_load_lds((const void*)(kb + rel + m.koff[i]),
+            __builtin_amdgcn_global_load_lds((const void*)(r.k + rel + m.kg[i]),
                                              (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
         if (do_v)
-            __builtin_amdgcn_global_load_lds((const void*)(vb + rel + m.voff[i]),
+            __builtin_amdgcn_global_load_lds((const void*)(r.v + rel + m.vg[i]),
                                              (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
     }
 }
+
+// Instruction-class masks of sched_group_barrier (AMDGPU backend).
+constexpr int kSgValu = 0x0002 | 0x0400;  // VALU, transcendentals included
+constexpr int kSgMfma = 0x0008;
+constexpr int kSgDsRead = 0x0100;
+// Ask the scheduler for `n` instructions of class `mask` next, in this order.
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -462,7 +470,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     }
 
     // ---- per-lane query row and its allowed key ranges
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
     const int l32 = lane & 31, h = lane >> 5;
     const int32_t row = r0 + wave * 32 + l32;
     const bool row_ok = row < c.q_tokens;
@@ -487,112 +496,216 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.0f;
     const float cs = c.scale * kLog2e;
-    const LoadMap<D> lm = load_map<D>();
+    const LoadMap<D> lm = load_map<D>(wave, (uint32_t)(c.heads * D * 2));
     const LdsAddr<D> la = lds_addr<D>(lane);
 
-    // ---- prologue: K(it0), V(it0) and K(it0+1) into LDS; S^T(it0)
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using NotLast = std::integral_constant<bool, false>;
+    using Last = std::integral_constant<bool, true>;
+
+    // Pipeline state between tiles: s = S^T(it) (raw dot products, masked),
+    // m_ref its exponent reference, pf[0][*] the bf16 weights of its first 32
+    // keys (computed early), l_run the weight sum so far (including them).
     f32x16 s[2];
     s[0] = f32x16{};
     s[1] = f32x16{};
+    bf16x8 pf0[2];
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+    // Mask S^T of tile `it` in place: nothing to do when every row of the wave
+    // allows the whole tile (always, except at the tail, for chunk attention).
+    auto mask_tile = [&](int32_t it) __attribute__((always_inline)) {
+        const int32_t j0 = tile_at(tr, it) * BK;
+        if (!c.moba.enabled && j0 + BK <= c.kv_total) return;
+        const uint32_t lane_full = (row_ok ? 0u : 1u) | ((uint32_t)(lo0 <= j0) & (uint32_t)(j0 + BK <= hi0)) |
+                                   ((uint32_t)(lo1 <= j0) & (uint32_t)(j0 + BK <= hi1));
+        if (__builtin_amdgcn_ballot_w64(lane_full == 0u) == 0) return;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int32_t j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const uint32_t ok = in_range(j, lo0, hi0) | in_range(j, lo1, hi1);
+                s[kb][r] = ok ? s[kb][r] : -INFINITY;
+            }
+    };
+
+    // Row max of the (masked) S^T and the new exponent reference: m_ref moves
+    // only when a row's tile max exceeds it by more than kTau (p <= 2^kTau).
+    // Returns alpha, the factor by which earlier O and l must be scaled.
+    auto new_ref = [&]() __attribute__((always_inline)) -> float {
+        float mx = s[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+        const float mt = pair_max(mx) * cs;
+        const bool grow = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
+        const float m_new = grow ? fmaxf(m_ref, mt) : m_ref;
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        m_ref = m_new;
+        return alpha;
+    };
+
+    // 8 weights of S^T register block (kb, t) -> bf16, and their sum
+    auto weights = [&](auto kb_c, auto t_c, float m_use, float& lsum) __attribute__((always_inline)) -> bf16x8 {
+        constexpr int kb = decltype(kb_c)::value, t = decltype(t_c)::value;
+        f32x8 e;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_use));
+        const bf16x8 p8 = __builtin_convertvector(e, bf16x8);
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+            const bf16x2 pp = {p8[2 * q2], p8[2 * q2 + 1]};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum, false);
+        }
+        return p8;
+    };
+
+    // ---- prologue: K(it0), V(it0) and K(it0+1) into LDS; S^T(it0) and its first weights
     if (it0 < it1) {
-        issue_tile<D>(c, head, tile_at(tr, it0), lm, kb0, vb0, true, true);
-        if (it0 + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it0 + 1), lm, kb1, vb1, true, false);
+        issue_tile<D>(c, head, tile_at(tr, it0), lm, wave, kb0, vb0, true, true);
+        if (it0 + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it0 + 1), lm, wave, kb1, vb1, true, false);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (wave_has_rows) qk_tile<D>(kb0, qf, la, s);
+        if (wave_has_rows) {
+            qk_tile<D>(kb0, qf, la, s);
+            mask_tile(it0);
+            new_ref();  // O and l are still zero
+            const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+            float lsum = 0.0f;
+            pf0[0] = weights(I0{}, I0{}, m_use, lsum);
+            pf0[1] = weights(I0{}, I1{}, m_use, lsum);
+            l_run = lsum;
+        }
         __syncthreads();  // K(it0) is read; the first iteration refills its buffer
     }
 
     // One key tile; ST (compile time) is the buffer holding K(it) and V(it);
     // K(it+1) is in the other K buffer.  Fills K(it+2) into K buffer ST and
-    // V(it+1) into the other V buffer while it computes.
-    auto step = [&](auto st_tag, int32_t it) {
+    // V(it+1) into the other V buffer while it computes.  LAST: no next tile.
+    auto step = [&](auto st_tag, auto last_tag, int32_t it) __attribute__((always_inline)) {
         constexpr int ST = decltype(st_tag)::value;
+        constexpr bool LAST = decltype(last_tag)::value;
         const Buf<D>& kcur = ST ? kb1 : kb0;
         const Buf<D>& knext = ST ? kb0 : kb1;
         const Buf<D>& vcur = ST ? vb1 : vb0;
         const Buf<D>& vnext = ST ? vb0 : vb1;
-        if (it + 2 < it1) issue_tile<D>(c, head, tile_at(tr, it + 2), lm, kcur, vcur, true, false);
-        if (it + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it + 1), lm, knext, vnext, false, true);
+        if (it + 2 < it1) issue_tile<D>(c, head, tile_at(tr, it + 2), lm, wave, kcur, vcur, true, false);
+        if (it + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it + 1), lm, wave, knext, vnext, false, true);
 
         if (wave_has_rows) {
-            const int32_t j0 = tile_at(tr, it) * BK;
-            // mask: skipped when every row of the wave allows the whole tile
-            const uint32_t lane_full = (row_ok ? 0u : 1u) | ((uint32_t)(lo0 <= j0) & (uint32_t)(j0 + BK <= hi0)) |
-                                       ((uint32_t)(lo1 <= j0) & (uint32_t)(j0 + BK <= hi1));
-            if (__builtin_amdgcn_ballot_w64(lane_full == 0u) != 0) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int32_t j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const uint32_t ok = in_range(j, lo0, hi0) | in_range(j, lo1, hi1);
-                        s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                    }
-            }
-
-            // online softmax: m_ref moves (and O, l rescale) only when a row's
-            // tile max exceeds it by more than kTau, so p <= 2^kTau
-            float mx = s[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-            const float mt = pair_max(mx) * cs;
-            if (__builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0) {
-                const float m_new = fmaxf(m_ref, mt);
-                const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-                l_run *= alpha;
-                m_ref = m_new;
-            }
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-
-            bf16x8 pf[2][2];
+            // [A] S^T(it+1) = K(it+1) Q^T on the matrix core, next to the second
+            //     half of this tile's weights on the VALU
+            bf16x8 pf1[2];
             float lsum = 0.0f;
-            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+            f32x16 sn0 = f32x16{}, sn1 = f32x16{};
+            if (!LAST) {
+                const char LDS_AS* kn0 = knext.template block_row<0>(0);
+                const char LDS_AS* kn1 = knext.template block_row<1>(0);
+                f32x8 e0, e1;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                for (int ds = 0; ds < C::DS; ++ds) {
+                    const bf16x8 a0 = *(const bf16x8 LDS_AS*)(kn0 + la.k[ds]);
+                    sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ds], sn0, 0, 0, 0);
+                    const bf16x8 a1 = *(const bf16x8 LDS_AS*)(kn1 + la.k[ds]);
+                    sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ds], sn1, 0, 0, 0);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    f32x8 e;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_use));
-                    pf[kb][t] = __builtin_convertvector(e, bf16x8);
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; ++q2) {
-                        const bf16x2 pp = {pf[kb][t][2 * q2], pf[kb][t][2 * q2 + 1]};
-                        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum, false);
+                    for (int x = 0; x < 16 / C::DS; ++x) {
+                        const int idx = ds * (16 / C::DS) + x;  // 0..15 over s[1]
+                        const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs, -m_use));
+                        if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
                     }
                 }
+                pf1[0] = __builtin_convertvector(e0, bf16x8);
+                pf1[1] = __builtin_convertvector(e1, bf16x8);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2) {
+                        const bf16x2 pp = {pf1[t][2 * q2], pf1[t][2 * q2 + 1]};
+                        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum, false);
+                    }
+                // keep these weights in this block (they are only used after the
+                // mask branch below, and would otherwise be sunk past it)
+                asm volatile("" ::"v"(pf1[0]), "v"(pf1[1]), "v"(lsum));
+                // schedule: K operands one k-step ahead, VALU work between MFMAs
+                sched_group(kSgDsRead, 2);
+#pragma unroll
+                for (int ds = 0; ds < C::DS; ++ds) {
+                    if (ds + 1 < C::DS) sched_group(kSgDsRead, 2);
+                    sched_group(kSgMfma, 1);
+                    sched_group(kSgValu, 3);
+                    sched_group(kSgMfma, 1);
+                    sched_group(kSgValu, 3);
+                }
+            } else {
+                pf1[0] = weights(I1{}, I0{}, m_use, lsum);
+                pf1[1] = weights(I1{}, I1{}, m_use, lsum);
             }
             l_run += lsum;
 
-            // S^T of the next tile: independent of the exponentials above
-            if (it + 1 < it1) qk_tile<D>(knext, qf, la, s);
-
-            // O^T += V^T P^T for this tile
+            // [B] O^T += V(it)^T P(it)^T on the matrix core, next to the row max,
+            //     the new reference and the first half of the weights of it+1
+            bf16x8 pn0[2];
+            float alpha = 1.0f, lsum_n = 0.0f;
+            if (!LAST) {
+                s[0] = sn0;
+                s[1] = sn1;
+                mask_tile(it + 1);
+            }
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+            for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 0>(vcur, la, db, t), pf[0][t], o[db],
-                                                                    0, 0, 0);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 1>(vcur, la, db, t), pf[1][t], o[db],
-                                                                    0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 0>(vcur, la, db, t), pf0[t], o[db], 0,
+                                                                    0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 1>(vcur, la, db, t), pf1[t], o[db], 0,
+                                                                    0, 0);
                 }
+            }
+            if (!LAST) {  // the scheduler interleaves these with the MFMAs above
+                alpha = new_ref();
+                const float m_next = (m_ref == -INFINITY) ? 0.0f : m_ref;
+                pn0[0] = weights(I0{}, I0{}, m_next, lsum_n);
+                pn0[1] = weights(I0{}, I1{}, m_next, lsum_n);
+            }
+            if (!LAST) asm volatile("" ::"v"(pn0[0]), "v"(pn0[1]), "v"(lsum_n), "v"(alpha));  // keep them here
+            // schedule: V^T reads two MFMAs ahead, VALU work between MFMAs
+            sched_group(kSgDsRead, 4);
+#pragma unroll
+            for (int i = 0; i < 4 * C::DB; ++i) {
+                if (i + 2 < 4 * C::DB) sched_group(kSgDsRead, 2);
+                sched_group(kSgMfma, 1);
+                sched_group(kSgValu, LAST ? 0 : 5);
+            }
+            if (!LAST) {
+                if (alpha != 1.0f) {  // rare: a row max grew by more than kTau
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+                }
+                l_run = l_run * alpha + lsum_n;
+                pf0[0] = pn0[0];
+                pf0[1] = pn0[1];
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
     int32_t it = it0;
-    for (; it + 1 < it1; it += 2) {
-        step(std::integral_constant<int, 0>{}, it);
-        step(std::integral_constant<int, 1>{}, it + 1);
+    for (; it + 2 < it1; it += 2) {
+        step(I0{}, NotLast{}, it);
+        step(I1{}, NotLast{}, it + 1);
     }
-    if (it < it1) step(std::integral_constant<int, 0>{}, it);
+    // one or two tiles left (or none)
+    if (it + 1 < it1) {
+        step(I0{}, NotLast{}, it);
+        step(I1{}, Last{}, it + 1);
+    } else if (it < it1) {
+        step(I0{}, Last{}, it);
+    }
 
     const float l_tot = pair_sum(l_run);
     __bf16* op = (__bf16*)c.out + (int64_t)row * stride + (int64_t)head * D;
