@@ -183,6 +183,12 @@ __device__ __forceinline__ int32_t tile_at(const TileRanges& r, int32_t it) {
     return it < n0 ? r.b0 + it : it < n1 ? r.b1 + (it - n0) : it < n2 ? r.b2 + (it - n1) : r.b3 + (it - n2);
 }
 
+// End (exclusive, in tiles) of the tile range that visit `it` falls in.
+__device__ __forceinline__ int32_t range_end_at(const TileRanges& r, int32_t it) {
+    const int32_t n0 = r.e0 - r.b0, n1 = n0 + (r.e1 - r.b1), n2 = n1 + (r.e2 - r.b2);
+    return it < n0 ? r.e0 : it < n1 ? r.e1 : it < n2 ? r.e2 : r.e3;
+}
+
 // Allowed key ranges of one query row (see wmk.h).
 __device__ __forceinline__ void row_ranges(const AttnCall& c, int32_t row, int32_t& lo0, int32_t& hi0, int32_t& lo1,
                                            int32_t& hi1) {
@@ -227,6 +233,44 @@ __device__ __forceinline__ SpanSel span_sel(const KvSpans& kv, int32_t j) {
     return r;
 }
 
+// Where the direct loads of one visited key tile come from.  `run` > 0: this
+// tile and the next run - 1 visited tiles lie in one tile range and wholly
+// inside one span, so each is one uniform base (k, v: the tile's first key row
+// of this head) plus per-lane offsets, and the next one is 64 rows further.
+// run <= 0: the tile crosses a span end or the last key (per-row lookup).
+// Advancing is a few scalar adds except where a run ends.
+struct Cursor {
+    int32_t tile;
+    int32_t run;
+    const char* k;
+    const char* v;
+};
+
+__device__ __forceinline__ Cursor cursor_at(const AttnCall& c, const TileRanges& tr, int32_t it, int64_t row_bytes,
+                                            int64_t head_off) {
+    Cursor cu;
+    cu.tile = tile_at(tr, it);
+    const int32_t j0 = cu.tile * BK;
+    const SpanSel sp = span_sel(c.kv, j0);
+    cu.run = min(range_end_at(tr, it) - cu.tile, (sp.end - j0) / BK);
+    const int64_t base = (int64_t)(j0 - sp.start) * row_bytes + head_off;
+    cu.k = sp.k + base;
+    cu.v = sp.v + base;
+    return cu;
+}
+
+__device__ __forceinline__ void advance(Cursor& cu, const AttnCall& c, const TileRanges& tr, int32_t it_next,
+                                        int64_t row_bytes, int64_t head_off) {
+    if (cu.run > 1) {
+        cu.tile += 1;
+        cu.run -= 1;
+        cu.k += BK * row_bytes;
+        cu.v += BK * row_bytes;
+    } else {
+        cu = cursor_at(c, tr, it_next, row_bytes, head_off);
+    }
+}
+
 // This thread's share of the direct tile loads: for each of its LPT wave loads
 // of a K (or V) tile, the key row inside the tile it fills and the byte offset
 // (from the tile's first key row of this head) of the swizzle-mapped source
@@ -269,37 +313,28 @@ struct Buf {
     }
 };
 
-// Issue the direct loads of key tile `tile` into LDS (kbuf and/or vbuf).
-// Common case: the tile lies inside one span -> uniform base + per-lane
-// offsets.  A tile crossing a span end or the last key looks up each row's
-// span; rows past the last key read the last key instead (finite data that
-// the mask drops).
+// Issue the direct loads of the key tile at cursor `cu` into LDS (kbuf and/or
+// vbuf).  Rows past the last key (only in a tile that crosses it) read the last
+// key instead: finite data that the mask drops.
 template <int D>
-__device__ __forceinline__ void issue_tile(const AttnCall& c, int32_t head, int32_t tile, const LoadMap<D>& m,
+__device__ __forceinline__ void issue_tile(const AttnCall& c, int32_t head, const Cursor& cu, const LoadMap<D>& m,
                                            int wave, const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
     using C = Cfg<D>;
-    const int64_t row_bytes = (int64_t)c.heads * D * 2;
-    const int64_t head_off = (int64_t)head * D * 2;
-    const int32_t j0 = tile * BK;
-    const SpanSel sp = span_sel(c.kv, j0);
-    if (j0 + BK <= sp.end) {
-        // whole tile inside one span: uniform base + per-lane constant offset
-        const int64_t base = (int64_t)(j0 - sp.start) * row_bytes + head_off;
-        const char* kb = sp.k + base;
-        const char* vb = sp.v + base;
+    if (cu.run > 0) {
 #pragma unroll
         for (int i = 0; i < C::LPT; ++i) {
             if (do_k)
-                __builtin_amdgcn_global_load_lds((const void*)(kb + m.kg[i]),
+                __builtin_amdgcn_global_load_lds((const void*)(cu.k + m.kg[i]),
                                                  (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
             if (do_v)
-                __builtin_amdgcn_global_load_lds((const void*)(vb + m.vg[i]),
+                __builtin_amdgcn_global_load_lds((const void*)(cu.v + m.vg[i]),
                                                  (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
         }
         return;
     }
-    // tile crossing a span end or the last key: per-row span; rows past the
-    // last key read the last key instead (finite data that the mask drops)
+    const int64_t row_bytes = (int64_t)c.heads * D * 2;
+    const int64_t head_off = (int64_t)head * D * 2;
+    const int32_t j0 = cu.tile * BK;
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
         const int32_t j = min(j0 + m.row[i], c.kv_total - 1);
@@ -515,8 +550,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
 
     // Mask S^T of tile `it` in place: nothing to do when every row of the wave
     // allows the whole tile (always, except at the tail, for chunk attention).
-    auto mask_tile = [&](int32_t it) __attribute__((always_inline)) {
-        const int32_t j0 = tile_at(tr, it) * BK;
+    auto mask_tile = [&](int32_t tile) __attribute__((always_inline)) {
+        const int32_t j0 = tile * BK;
         if (!c.moba.enabled && j0 + BK <= c.kv_total) return;
         const uint32_t lane_full = (row_ok ? 0u : 1u) | ((uint32_t)(lo0 <= j0) & (uint32_t)(j0 + BK <= hi0)) |
                                    ((uint32_t)(lo1 <= j0) & (uint32_t)(j0 + BK <= hi1));
@@ -564,14 +599,21 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     };
 
     // ---- prologue: K(it0), V(it0) and K(it0+1) into LDS; S^T(it0) and its first weights
+    // Cursors: vcu at the tile whose V is loaded next (it+1 in step it), kcu two ahead.
+    const int64_t row_bytes = (int64_t)c.heads * D * 2;
+    const int64_t head_off = (int64_t)head * D * 2;
+    Cursor vcu = cursor_at(c, tr, it0, row_bytes, head_off);
+    const int32_t tile0 = vcu.tile;
+    Cursor kcu = vcu;
     if (it0 < it1) {
-        issue_tile<D>(c, head, tile_at(tr, it0), lm, wave, kb0, vb0, true, true);
-        if (it0 + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it0 + 1), lm, wave, kb1, vb1, true, false);
+        issue_tile<D>(c, head, vcu, lm, wave, kb0, vb0, true, true);
+        advance(vcu, c, tr, it0 + 1, row_bytes, head_off);
+        if (it0 + 1 < it1) issue_tile<D>(c, head, vcu, lm, wave, kb1, vb1, true, false);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (wave_has_rows) {
             qk_tile<D>(kb0, qf, la, s);
-            mask_tile(it0);
+            mask_tile(tile0);
             new_ref();  // O and l are still zero
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
             float lsum = 0.0f;
@@ -581,6 +623,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
         }
         __syncthreads();  // K(it0) is read; the first iteration refills its buffer
     }
+    kcu = vcu;
+    advance(kcu, c, tr, it0 + 2, row_bytes, head_off);
 
     // One key tile; ST (compile time) is the buffer holding K(it) and V(it);
     // K(it+1) is in the other K buffer.  Fills K(it+2) into K buffer ST and
@@ -592,8 +636,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
         const Buf<D>& knext = ST ? kb0 : kb1;
         const Buf<D>& vcur = ST ? vb1 : vb0;
         const Buf<D>& vnext = ST ? vb0 : vb1;
-        if (it + 2 < it1) issue_tile<D>(c, head, tile_at(tr, it + 2), lm, wave, kcur, vcur, true, false);
-        if (it + 1 < it1) issue_tile<D>(c, head, tile_at(tr, it + 1), lm, wave, knext, vnext, false, true);
+        if (it + 2 < it1) issue_tile<D>(c, head, kcu, lm, wave, kcur, vcur, true, false);
+        if (it + 1 < it1) issue_tile<D>(c, head, vcu, lm, wave, knext, vnext, false, true);
+        const int32_t tile_next = vcu.tile;
+        vcu = kcu;
+        advance(kcu, c, tr, it + 3, row_bytes, head_off);
 
         if (wave_has_rows) {
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -654,7 +701,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
             if (!LAST) {
                 s[0] = sn0;
                 s[1] = sn1;
-                mask_tile(it + 1);
+                mask_tile(tile_next);
             }
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) {
