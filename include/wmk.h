@@ -59,7 +59,7 @@ typedef enum { WMK_F32 = 0, WMK_BF16 = 1 } wmk_dtype;
  * chunk being generated. */
 typedef struct {
     int32_t num_layers;       /* >= 1                                                  */
-    int32_t num_heads;        /* >= 1                                                  */
+    int32_t num_heads;        /* 1 .. 4096                                             */
     int32_t head_dim;         /* 64 or 128                                             */
     int32_t tokens_per_frame; /* >= 1 (1508 for a 52x29 latent grid)                   */
     int32_t sink_frames;      /* S >= 0                                                */
@@ -71,8 +71,8 @@ typedef struct {
 typedef struct wmk_cache wmk_cache; /* opaque host handle */
 
 typedef struct {
-    int32_t num_heads;
-    int32_t head_dim; /* 64 or 128 */
+    int32_t num_heads; /* 1 .. 4096 */
+    int32_t head_dim;  /* 64 or 128 */
     wmk_dtype dtype;
 } wmk_head_desc;
 

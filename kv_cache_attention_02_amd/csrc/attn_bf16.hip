@@ -42,6 +42,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "wmk_internal.h"
 
@@ -313,39 +314,64 @@ struct Buf {
     }
 };
 
+// Buffer resource over `bytes` bytes from `base` (raw: byte offsets, no
+// stride); lanes whose offset falls outside read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct load of 16 bytes per lane at byte offset `off` of buffer `r` into the
+// 1 KB block of this wave in LDS object `dst`.  Buffer (not global) loads: the
+// compiler counts these only on the vector-memory counter, so waits for LDS
+// reads that follow need not drain them.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, char LDS_AS* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, off, 0, 0, 0);
+}
+
 // Issue the direct loads of the key tile at cursor `cu` into LDS (kbuf and/or
-// vbuf).  Rows past the last key (only in a tile that crosses it) read the last
-// key instead: finite data that the mask drops.
+// vbuf).  Common case: the tile lies inside one span, so one buffer resource
+// starting at its first row and per-lane constant offsets.  A tile crossing a
+// span end (or the last key) loads each span's rows under a lane mask; rows
+// past the last key read the last key instead (finite data that the mask
+// drops).
 template <int D>
 __device__ __forceinline__ void issue_tile(const AttnCall& c, int32_t head, const Cursor& cu, const LoadMap<D>& m,
                                            int wave, const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
     using C = Cfg<D>;
+    const int64_t row_bytes = (int64_t)c.heads * D * 2;
+    const uint32_t tile_bytes = (uint32_t)(BK * row_bytes);  // < 2^31: checked on the host
     if (cu.run > 0) {
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(cu.k, tile_bytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(cu.v, tile_bytes);
 #pragma unroll
         for (int i = 0; i < C::LPT; ++i) {
-            if (do_k)
-                __builtin_amdgcn_global_load_lds((const void*)(cu.k + m.kg[i]),
-                                                 (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
-            if (do_v)
-                __builtin_amdgcn_global_load_lds((const void*)(cu.v + m.vg[i]),
-                                                 (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
+            if (do_k) dma16(rk, m.kg[i], kbuf.part[i] + wave * 1024);
+            if (do_v) dma16(rv, m.vg[i], vbuf.part[i] + wave * 1024);
         }
         return;
     }
-    const int64_t row_bytes = (int64_t)c.heads * D * 2;
+    // per span touched by the tile: a resource from the span's first row in
+    // the tile, and a lane mask for the rows in that span
     const int64_t head_off = (int64_t)head * D * 2;
-    const int32_t j0 = cu.tile * BK;
+    const int32_t j0 = cu.tile * BK, j1 = min(j0 + BK, c.kv_total);
+#pragma nounroll
+    for (int x = 0; x < c.kv.n; ++x) {
+        const int32_t sb = x == 0 ? 0 : c.kv.end[x - 1], se = c.kv.end[x];
+        if (se <= j0 || sb >= j1) continue;  // tile does not touch span x
+        const int32_t r0 = max(j0, sb);      // first key of the span in this tile
+        const int64_t base = (int64_t)(r0 - sb) * row_bytes + head_off;
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((const char*)c.kv.k[x] + base, tile_bytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((const char*)c.kv.v[x] + base, tile_bytes);
 #pragma unroll
-    for (int i = 0; i < C::LPT; ++i) {
-        const int32_t j = min(j0 + m.row[i], c.kv_total - 1);
-        const SpanSel r = span_sel(c.kv, j);
-        const int64_t rel = (int64_t)(j - r.start) * row_bytes + head_off - (int64_t)m.row[i] * row_bytes;
-        if (do_k)
-            __builtin_amdgcn_global_load_lds((const void*)(r.k + rel + m.kg[i]),
-                                             (void LDS_AS*)(kbuf.part[i] + wave * 1024), 16, 0, 0);
-        if (do_v)
-            __builtin_amdgcn_global_load_lds((const void*)(r.v + rel + m.vg[i]),
-                                             (void LDS_AS*)(vbuf.part[i] + wave * 1024), 16, 0, 0);
+        for (int i = 0; i < C::LPT; ++i) {
+            const int32_t j = min(j0 + m.row[i], c.kv_total - 1);
+            if (j >= sb && j < se) {
+                // (j - r0) rows below the resource start, at this lane's chunk
+                const uint32_t off = (uint32_t)((j - r0) - m.row[i]) * (uint32_t)row_bytes;
+                if (do_k) dma16(rk, off + m.kg[i], kbuf.part[i] + wave * 1024);
+                if (do_v) dma16(rv, off + m.vg[i], vbuf.part[i] + wave * 1024);
+            }
+        }
     }
 }
 
@@ -645,95 +671,140 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
         if (wave_has_rows) {
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
             // [A] S^T(it+1) = K(it+1) Q^T on the matrix core, next to the second
-            //     half of this tile's weights on the VALU
-            bf16x8 pf1[2];
-            float lsum = 0.0f;
+            //     half of this tile's weights (pf1) on the VALU.  The order is
+            //     written out: K fragments KPF k-steps ahead, and a scheduling
+            //     fence after each k-step keeps it.
+            constexpr int KPF = 2;
+            constexpr int EPS = 16 / C::DS;  // weights of s[1] per k-step
             f32x16 sn0 = f32x16{}, sn1 = f32x16{};
-            if (!LAST) {
+            f32x8 e0, e1;
+            if constexpr (!LAST) {
                 const char LDS_AS* kn0 = knext.template block_row<0>(0);
                 const char LDS_AS* kn1 = knext.template block_row<1>(0);
-                f32x8 e0, e1;
+                bf16x8 ka[KPF + 1][2];
+#pragma unroll
+                for (int d = 0; d < KPF; ++d) {
+                    ka[d][0] = *(const bf16x8 LDS_AS*)(kn0 + la.k[d]);
+                    ka[d][1] = *(const bf16x8 LDS_AS*)(kn1 + la.k[d]);
+                }
 #pragma unroll
                 for (int ds = 0; ds < C::DS; ++ds) {
-                    const bf16x8 a0 = *(const bf16x8 LDS_AS*)(kn0 + la.k[ds]);
-                    sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ds], sn0, 0, 0, 0);
-                    const bf16x8 a1 = *(const bf16x8 LDS_AS*)(kn1 + la.k[ds]);
-                    sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ds], sn1, 0, 0, 0);
+                    if (ds + KPF < C::DS) {
+                        ka[(ds + KPF) % (KPF + 1)][0] = *(const bf16x8 LDS_AS*)(kn0 + la.k[ds + KPF]);
+                        ka[(ds + KPF) % (KPF + 1)][1] = *(const bf16x8 LDS_AS*)(kn1 + la.k[ds + KPF]);
+                    }
+                    sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][0], qf[ds], sn0, 0, 0, 0);
 #pragma unroll
-                    for (int x = 0; x < 16 / C::DS; ++x) {
-                        const int idx = ds * (16 / C::DS) + x;  // 0..15 over s[1]
+                    for (int x = 0; x < EPS; ++x) {
+                        const int idx = ds * EPS + x;
                         const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs, -m_use));
                         if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
                     }
-                }
-                pf1[0] = __builtin_convertvector(e0, bf16x8);
-                pf1[1] = __builtin_convertvector(e1, bf16x8);
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; ++q2) {
-                        const bf16x2 pp = {pf1[t][2 * q2], pf1[t][2 * q2 + 1]};
-                        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum, false);
-                    }
-                // keep these weights in this block (they are only used after the
-                // mask branch below, and would otherwise be sunk past it)
-                asm volatile("" ::"v"(pf1[0]), "v"(pf1[1]), "v"(lsum));
-                // schedule: K operands one k-step ahead, VALU work between MFMAs
-                sched_group(kSgDsRead, 2);
-#pragma unroll
-                for (int ds = 0; ds < C::DS; ++ds) {
-                    if (ds + 1 < C::DS) sched_group(kSgDsRead, 2);
-                    sched_group(kSgMfma, 1);
-                    sched_group(kSgValu, 3);
-                    sched_group(kSgMfma, 1);
-                    sched_group(kSgValu, 3);
+                    sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][1], qf[ds], sn1, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
-                pf1[0] = weights(I1{}, I0{}, m_use, lsum);
-                pf1[1] = weights(I1{}, I1{}, m_use, lsum);
+#pragma unroll
+                for (int idx = 0; idx < 16; ++idx) {
+                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs, -m_use));
+                    if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
+                }
             }
+            bf16x8 pf1[2];
+            pf1[0] = __builtin_convertvector(e0, bf16x8);
+            pf1[1] = __builtin_convertvector(e1, bf16x8);
+            float lsum = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) {
+                    const bf16x2 pp = {pf1[t][2 * q2], pf1[t][2 * q2 + 1]};
+                    lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum, false);
+                }
+            // keep these weights here: they are only used after the mask branch
+            // below, and would otherwise be sunk past it
+            asm volatile("" ::"v"(pf1[0]), "v"(pf1[1]), "v"(lsum));
             l_run += lsum;
 
-            // [B] O^T += V(it)^T P(it)^T on the matrix core, next to the row max,
-            //     the new reference and the first half of the weights of it+1
-            bf16x8 pn0[2];
-            float alpha = 1.0f, lsum_n = 0.0f;
-            if (!LAST) {
+            // [B] O^T += V(it)^T P(it)^T on the matrix core (V^T fragments VPF
+            //     MFMAs ahead), next to the row max of S^T(it+1), the new
+            //     reference and the first half of its weights (pn0) on the VALU,
+            //     spread over the MFMAs by hand and fenced like [A].
+            if constexpr (!LAST) {
                 s[0] = sn0;
                 s[1] = sn1;
                 mask_tile(tile_next);
             }
+            constexpr int NPV = 4 * C::DB;   // PV MFMAs: (db, t, kb)
+            constexpr int VPF = 3;
+            constexpr int RMX = NPV / 4;     // slots of the max reduction
+            constexpr int SREF = RMX;        // slot of the new reference
+            constexpr int WFIRST = RMX + 1;  // weights in slots WFIRST .. NPV - 2
+            constexpr int WSLOTS = NPV - 1 - WFIRST;
+            auto vfrag_at = [&](auto i_c) __attribute__((always_inline)) -> bf16x8 {
+                constexpr int i = decltype(i_c)::value;
+                if constexpr (i % 2 == 0) return v_frag<D, 0>(vcur, la, i / 4, (i / 2) % 2);
+                else return v_frag<D, 1>(vcur, la, i / 4, (i / 2) % 2);
+            };
+            bf16x8 vfr[VPF + 1];
+            [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
+                ((vfr[I] = vfrag_at(std::integral_constant<int, I>{})), ...);
+            }(std::make_integer_sequence<int, VPF>{});
+            float mx = -INFINITY, alpha = 1.0f, m_next = 0.0f, lsum_n = 0.0f;
+            bool grow = false;
+            f32x8 w0, w1;
+            bf16x8 pn0[2];
+            [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
+                auto slot = [&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    if constexpr (i + VPF < NPV) vfr[(i + VPF) % (VPF + 1)] = vfrag_at(std::integral_constant<int, i + VPF>{});
+                    constexpr int db = i / 4, t = (i / 2) % 2, kb = i % 2;
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[i % (VPF + 1)], kb ? pf1[t] : pf0[t], o[db],
+                                                                    0, 0, 0);
+                    if constexpr (!LAST) {
+                        if constexpr (i < RMX) {  // row max of S^T(it+1), 32 / RMX values per slot
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
+                            for (int r = i * (32 / RMX); r < (i + 1) * (32 / RMX); ++r) mx = fmaxf(mx, s[r / 16][r % 16]);
+                        } else if constexpr (i == SREF) {
+                            const float mt = pair_max(mx) * cs;
+                            grow = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
+                            const float m_new = grow ? fmaxf(m_ref, mt) : m_ref;
+                            alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                            m_ref = m_new;
+                            m_next = (m_new == -INFINITY) ? 0.0f : m_new;
+                        } else if constexpr (i >= WFIRST && i < NPV - 1) {  // weights of s[0]
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 0>(vcur, la, db, t), pf0[t], o[db], 0,
-                                                                    0, 0);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag<D, 1>(vcur, la, db, t), pf1[t], o[db], 0,
-                                                                    0, 0);
-                }
-            }
-            if (!LAST) {  // the scheduler interleaves these with the MFMAs above
-                alpha = new_ref();
-                const float m_next = (m_ref == -INFINITY) ? 0.0f : m_ref;
-                pn0[0] = weights(I0{}, I0{}, m_next, lsum_n);
-                pn0[1] = weights(I0{}, I1{}, m_next, lsum_n);
-            }
-            if (!LAST) asm volatile("" ::"v"(pn0[0]), "v"(pn0[1]), "v"(lsum_n), "v"(alpha));  // keep them here
-            // schedule: V^T reads two MFMAs ahead, VALU work between MFMAs
-            sched_group(kSgDsRead, 4);
+                            for (int r = 0; r < 16; ++r)
+                                if (WFIRST + r * WSLOTS / 16 == i) {
+                                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], cs, -m_next));
+                                    if (r < 8) w0[r] = v; else w1[r - 8] = v;
+                                }
+                        } else if constexpr (i == NPV - 1) {
+                            pn0[0] = __builtin_convertvector(w0, bf16x8);
+                            pn0[1] = __builtin_convertvector(w1, bf16x8);
 #pragma unroll
-            for (int i = 0; i < 4 * C::DB; ++i) {
-                if (i + 2 < 4 * C::DB) sched_group(kSgDsRead, 2);
-                sched_group(kSgMfma, 1);
-                sched_group(kSgValu, LAST ? 0 : 5);
-            }
-            if (!LAST) {
-                if (alpha != 1.0f) {  // rare: a row max grew by more than kTau
+                            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                                for (int q2 = 0; q2 < 4; ++q2) {
+                                    const bf16x2 pp = {pn0[t2][2 * q2], pn0[t2][2 * q2 + 1]};
+                                    lsum_n = __builtin_amdgcn_fdot2_f32_bf16(pp, one2, lsum_n, false);
+                                }
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                };
+                (slot(std::integral_constant<int, I>{}), ...);
+            }(std::make_integer_sequence<int, NPV>{});
+            if constexpr (!LAST) {
+                // keep the next tile's weights in the slots above (they are only
+                // used after the branch below, and would otherwise be sunk past it)
+                asm volatile("" ::"v"(pn0[0]), "v"(pn0[1]), "v"(lsum_n), "v"(alpha));
+                if (grow) {  // rare: a row max grew by more than kTau
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+                    l_run *= alpha;
                 }
-                l_run = l_run * alpha + lsum_n;
+                l_run += lsum_n;
                 pf0[0] = pn0[0];
                 pf0[1] = pn0[1];
             }

@@ -88,6 +88,7 @@ wmk_status check_desc(const wmk_cache_desc* d) {
                     d->chunk_frames);
     if (d->head_dim != 64 && d->head_dim != 128)
         return fail(WMK_ERR_SHAPE, "head_dim %d is not 64 or 128", d->head_dim);
+    if (d->num_heads > wmk::kMaxHeads) return fail(WMK_ERR_SHAPE, "num_heads %d > %d", d->num_heads, wmk::kMaxHeads);
     const int64_t slots = (int64_t)d->sink_frames + d->window_frames;
     if (slots * d->tokens_per_frame > INT32_MAX)
         return fail(WMK_ERR_SHAPE, "(S + W) * tokens_per_frame exceeds 2^31 - 1 tokens");
@@ -98,6 +99,7 @@ wmk_status check_head(const wmk_head_desc* hd) {
     if (hd == nullptr) return fail(WMK_ERR_NULL, "head descriptor is NULL");
     if (!dtype_ok(hd->dtype)) return fail(WMK_ERR_DTYPE, "dtype %d is not WMK_F32 or WMK_BF16", (int)hd->dtype);
     if (hd->num_heads < 1) return fail(WMK_ERR_SHAPE, "num_heads %d < 1", hd->num_heads);
+    if (hd->num_heads > wmk::kMaxHeads) return fail(WMK_ERR_SHAPE, "num_heads %d > %d", hd->num_heads, wmk::kMaxHeads);
     if (hd->head_dim != 64 && hd->head_dim != 128)
         return fail(WMK_ERR_SHAPE, "head_dim %d is not 64 or 128", hd->head_dim);
     return WMK_OK;

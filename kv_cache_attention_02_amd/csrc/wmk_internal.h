@@ -10,6 +10,7 @@ namespace wmk {
 constexpr int kMaxSeg = 5;        // cache prefix + up to 4 caller segments
 constexpr int kMaxGroups = 64;    // q-tile groups of a longest-first launch order
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kMaxHeads = 4096;   // a 64-key tile of all heads stays below 2^31 bytes (32-bit buffer offsets)
 
 // Keys/values seen by one attention call: the virtual concatenation of up to
 // kMaxSeg spans, each [tokens][heads][head_dim].  seg_end is the exclusive

@@ -73,6 +73,7 @@ def test_cache_bytes(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(D=96), wmk.WMK_ERR_SHAPE), (dict(W=0), wmk.WMK_ERR_SHAPE), (dict(H=0), wmk.WMK_ERR_SHAPE),
+    (dict(H=4097), wmk.WMK_ERR_SHAPE),
     (dict(dtype=5), wmk.WMK_ERR_DTYPE), (dict(S=-2), wmk.WMK_ERR_SHAPE), (dict(cf=0), wmk.WMK_ERR_SHAPE),
 ])
 def test_init_rejects_bad_descriptor(lib, kw, status):
