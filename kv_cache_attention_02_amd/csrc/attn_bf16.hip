@@ -480,6 +480,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     __shared__ __attribute__((aligned(1024))) char v0p1[C::LPT > 1 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char v1p0[C::PARTB];
     __shared__ __attribute__((aligned(1024))) char v1p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char dummy[NW * 1024];  // sink of loads that fetch nothing
     static_assert(C::LPT <= 2, "at most two LDS objects per buffer");
     auto mkbuf = [](char* p0, char* p1) {
         Buf<D> b;
@@ -628,6 +629,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     // Cursors: vcu at the tile whose V is loaded next (it+1 in step it), kcu two ahead.
     const int64_t row_bytes = (int64_t)c.heads * D * 2;
     const int64_t head_off = (int64_t)head * D * 2;
+    const uint32_t tile_bytes = (uint32_t)(BK * row_bytes);
     Cursor vcu = cursor_at(c, tr, it0, row_bytes, head_off);
     const int32_t tile0 = vcu.tile;
     Cursor kcu = vcu;
@@ -662,11 +664,34 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
         const Buf<D>& knext = ST ? kb0 : kb1;
         const Buf<D>& vcur = ST ? vb1 : vb0;
         const Buf<D>& vnext = ST ? vb0 : vb1;
-        if (it + 2 < it1) issue_tile<D>(c, head, kcu, lm, wave, kcur, vcur, true, false);
-        if (it + 1 < it1) issue_tile<D>(c, head, vcu, lm, wave, knext, vnext, false, true);
+        // K(it+2) into kcur and V(it+1) into vnext, both read last in the
+        // previous step; spread over the MFMAs of [A] (the tile interface is
+        // busy for a while with each direct load, and a wave that issues all of
+        // them at once stalls).  A tile crossing a span end is loaded here,
+        // per span; its pieces then fetch nothing (zero-size resource) into a
+        // dummy block, as do those of a tile past the range.
+        const bool k_ok = it + 2 < it1, v_ok = it + 1 < it1;
+        const bool k_fast = k_ok && kcu.run > 0, v_fast = v_ok && vcu.run > 0;
+        if (k_ok && !k_fast) issue_tile<D>(c, head, kcu, lm, wave, kcur, vnext, true, false);
+        if (v_ok && !v_fast) issue_tile<D>(c, head, vcu, lm, wave, kcur, vnext, false, true);
+        const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kcu.k, k_fast ? tile_bytes : 0u);
+        const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vcu.v, v_fast ? tile_bytes : 0u);
+        auto k_piece = [&](int i) __attribute__((always_inline)) {
+            dma16(krs, lm.kg[i], (k_fast ? kcur.part[i] : (char LDS_AS*)dummy) + wave * 1024);
+        };
+        auto v_piece = [&](int i) __attribute__((always_inline)) {
+            dma16(vrs, lm.vg[i], (v_fast ? vnext.part[i] : (char LDS_AS*)dummy) + wave * 1024);
+        };
         const int32_t tile_next = vcu.tile;
         vcu = kcu;
         advance(kcu, c, tr, it + 3, row_bytes, head_off);
+        if (!wave_has_rows && !LAST) {
+#pragma unroll
+            for (int i = 0; i < C::LPT; ++i) {
+                k_piece(i);
+                v_piece(i);
+            }
+        }
 
         if (wave_has_rows) {
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -694,6 +719,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
                         ka[(ds + KPF) % (KPF + 1)][1] = *(const bf16x8 LDS_AS*)(kn1 + la.k[ds + KPF]);
                     }
                     sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][0], qf[ds], sn0, 0, 0, 0);
+                    if (ds % 4 == 1 && ds / 4 < C::LPT) k_piece(ds / 4);  // K pieces at ds 1, 5; V at 3, 7
+                    if (ds % 4 == 3 && ds / 4 < C::LPT) v_piece(ds / 4);
 #pragma unroll
                     for (int x = 0; x < EPS; ++x) {
                         const int idx = ds * EPS + x;
