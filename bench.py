@@ -267,6 +267,24 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps):
     avg, mn = timed(lambda: wmk.chunk_attention(None, 0, q, [(ke, ve), (kl, vl)], out=o))
     res["720p_cross"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(cflops / avg / 1e9, 1),
                          "frac_peak": round(cflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    del c, q, k, v, o
+    torch.cuda.empty_cache()
+
+    # chunk-causal cross-attention over a training sequence: the MoBA shape's 7
+    # chunks of 3 frames x 1560 tokens, each reading a 512-token environment
+    # prompt and its own 512-token local prompt (12 heads)
+    tpf, heads, cq, nc, ne, nl = 1560, 12, 3 * 1560, 7, 512, 512
+    q = fill((cq * nc, heads, D), kind=synth.Q)
+    kx = fill((ne + nc * nl, heads, D), kind=synth.KLOC)
+    vx = fill((ne + nc * nl, heads, D), kind=synth.VLOC)
+    o = torch.empty_like(q)
+    xflops = 4.0 * D * heads * cq * nc * (ne + nl)
+    avg, mn = timed(lambda: wmk.cross_attention_train(q, kx, vx, chunk_q_tokens=cq, env_tokens=ne, local_tokens=nl,
+                                                      out=o))
+    res["cross_train_32760"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4),
+                                "tflops": round(xflops / avg / 1e9, 1),
+                                "frac_peak": round(xflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                "q_tokens": cq * nc, "kv_tokens": ne + nc * nl}
     return res
 
 

@@ -94,6 +94,18 @@ typedef struct {
     int32_t bidir_block;      /* 1: append the bidirectional block; 0: clean + noisy only */
 } wmk_moba_desc;
 
+/* Chunk-causal cross-attention over a multi-chunk training sequence: queries
+ * are `chunks` chunks of `chunk_q_tokens` tokens each (chunk i = rows
+ * [i * chunk_q_tokens, (i + 1) * chunk_q_tokens)); keys/values are the shared
+ * environment prompt followed by one local prompt per chunk,
+ * [env_tokens | local_0 | local_1 | ...] with local_tokens tokens each. */
+typedef struct {
+    int32_t chunk_q_tokens; /* >= 1 */
+    int32_t chunks;         /* >= 1 */
+    int32_t env_tokens;     /* >= 0 */
+    int32_t local_tokens;   /* >= 0; env_tokens + local_tokens >= 1 */
+} wmk_xattn_desc;
+
 /* Bytes of the K buffer (equal to the V buffer) for all layers of a cache with
  * descriptor d: num_layers * (S + W) * tokens_per_frame * heads * head_dim *
  * sizeof(dtype).  Layout [layer][slot][tokens_per_frame][heads][head_dim].
@@ -170,6 +182,22 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
 wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
                               const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
+
+/* Chunk-causal cross-attention forward over a multi-chunk sequence (the
+ * training form of the chunk-wise prompt conditioning: "Infinite Worlds with
+ * Versatile Interactions", causal pretraining paragraph -- a causal
+ * cross-attention mask keeps chunk-wise prompts from leaking future
+ * semantics; "Mix Forcing", "Condition each chunk").  Query chunk i attends
+ * the environment prompt and its own local prompt i, nothing else; the local
+ * prompts of other chunks -- earlier or later -- are masked.
+ * q and out: [chunks * chunk_q_tokens][heads][head_dim]; k and v:
+ * [env_tokens + chunks * local_tokens][heads][head_dim]; dtype of hd.
+ * workspace as for wmk_chunk_attention.  Errors as for wmk_chunk_attention,
+ * plus a NULL descriptor -> WMK_ERR_NULL and a field out of its range, or more
+ * than 2^31 - 1 query or key tokens -> WMK_ERR_SHAPE. */
+wmk_status wmk_cross_attention_train(const wmk_xattn_desc* x, const wmk_head_desc* hd, const void* q,
+                                     const void* k, const void* v, void* out, float scale, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
 
 /* Message of the last error on the calling thread ("" if none); valid until
  * the next wmk call on that thread. */

@@ -44,6 +44,11 @@ class wmk_moba_desc(ctypes.Structure):
                 ("bidir_block", ctypes.c_int32)]
 
 
+class wmk_xattn_desc(ctypes.Structure):
+    _fields_ = [("chunk_q_tokens", ctypes.c_int32), ("chunks", ctypes.c_int32), ("env_tokens", ctypes.c_int32),
+                ("local_tokens", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _SIGNATURES = {
     "wmk_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_cache_desc)]),
@@ -58,6 +63,8 @@ _SIGNATURES = {
                                            ctypes.c_size_t, _P]),
     "wmk_moba_attention": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P, _P, _P,
                                           _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "wmk_cross_attention_train": (ctypes.c_int, [ctypes.POINTER(wmk_xattn_desc), ctypes.POINTER(wmk_head_desc), _P,
+                                                 _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "wmk_last_error": (ctypes.c_char_p, []),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -229,4 +236,30 @@ def moba_attention(q, k, v, *, tokens_per_frame, frames, chunk_frames, bidir_blo
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(load().wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                      scale, None, 0, _stream_ptr(stream)))
+    return out
+
+
+def cross_attention_train(q, k, v, *, chunk_q_tokens, env_tokens, local_tokens, out=None, scale=None,
+                          use_workspace=True, stream=None):
+    """Chunk-causal cross-attention over a multi-chunk sequence: query chunk i
+    (rows [i * chunk_q_tokens, (i + 1) * chunk_q_tokens)) reads keys
+    [0, env_tokens) and its own local prompt [env_tokens + i * local_tokens, +local_tokens)."""
+    torch = _torch()
+    nq, H, D = q.shape
+    if chunk_q_tokens <= 0 or nq % chunk_q_tokens:
+        raise ValueError(f"{nq} query tokens are not a whole number of chunks of {chunk_q_tokens}")
+    chunks = nq // chunk_q_tokens
+    if out is None:
+        out = torch.empty_like(q)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    xd = wmk_xattn_desc(chunk_q_tokens, chunks, env_tokens, local_tokens)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    ws, wsb = ctypes.c_void_p(0), 0
+    if use_workspace:
+        wsb = load().wmk_attention_workspace_bytes(ctypes.byref(hd), nq)
+        if wsb:
+            w = workspace(q.device, wsb)
+            ws, wsb = _ptr(w), w.numel()
+    _check(load().wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(out), scale, ws, wsb, _stream_ptr(stream)))
     return out

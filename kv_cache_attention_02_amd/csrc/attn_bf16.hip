@@ -134,11 +134,15 @@ __device__ __forceinline__ void emit(TileRanges& r, int k, int32_t b, int32_t e)
 
 __device__ __forceinline__ TileRanges tile_ranges(const AttnCall& c, int32_t r0, int32_t r1) {
     int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
-    if (!c.moba.enabled) {
+    if (c.mask.mode == kMaskNone) {
         set_tiles(l0, h0, 0, c.kv_total);
+    } else if (c.mask.mode == kMaskCross) {  // environment prompt + the local prompts of the tile's chunks
+        const int32_t ca = r0 / c.mask.part_len, cb = (r1 - 1) / c.mask.part_len;
+        set_tiles(l0, h0, 0, c.mask.env_len);
+        set_tiles(l1, h1, c.mask.env_len + ca * c.mask.chunk_len, c.mask.env_len + (cb + 1) * c.mask.chunk_len);
     } else {
-        const int32_t L = c.moba.part_len, cl = c.moba.chunk_len;
-        const int32_t pa = r0 / L, pb = min((r1 - 1) / L, c.moba.parts - 1);
+        const int32_t L = c.mask.part_len, cl = c.mask.chunk_len;
+        const int32_t pa = r0 / L, pb = min((r1 - 1) / L, c.mask.parts - 1);
         if (pa <= 0 && 0 <= pb) {  // clean rows: block-causal prefix
             const int32_t fb = min(r1, L) - 1;
             set_tiles(l0, h0, 0, min((fb / cl + 1) * cl, L));
@@ -194,8 +198,14 @@ __device__ __forceinline__ int32_t range_end_at(const TileRanges& r, int32_t it)
 __device__ __forceinline__ void row_ranges(const AttnCall& c, int32_t row, int32_t& lo0, int32_t& hi0, int32_t& lo1,
                                            int32_t& hi1) {
     lo1 = 0; hi1 = 0;
-    if (!c.moba.enabled || row >= c.q_tokens) { lo0 = 0; hi0 = c.kv_total; return; }
-    const int32_t L = c.moba.part_len, cl = c.moba.chunk_len;
+    if (c.mask.mode == kMaskNone || row >= c.q_tokens) { lo0 = 0; hi0 = c.kv_total; return; }
+    if (c.mask.mode == kMaskCross) {
+        const int32_t ch = row / c.mask.part_len;
+        lo0 = 0; hi0 = c.mask.env_len;
+        lo1 = c.mask.env_len + ch * c.mask.chunk_len; hi1 = lo1 + c.mask.chunk_len;
+        return;
+    }
+    const int32_t L = c.mask.part_len, cl = c.mask.chunk_len;
     const int32_t part = row / L, r = row - part * L, k = r / cl;
     const int32_t e = min((k + 1) * cl, L);
     if (part == 0) { lo0 = 0; hi0 = e; }
@@ -579,7 +589,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
     // allows the whole tile (always, except at the tail, for chunk attention).
     auto mask_tile = [&](int32_t tile) __attribute__((always_inline)) {
         const int32_t j0 = tile * BK;
-        if (!c.moba.enabled && j0 + BK <= c.kv_total) return;
+        if (c.mask.mode == kMaskNone && j0 + BK <= c.kv_total) return;
         const uint32_t lane_full = (row_ok ? 0u : 1u) | ((uint32_t)(lo0 <= j0) & (uint32_t)(j0 + BK <= hi0)) |
                                    ((uint32_t)(lo1 <= j0) & (uint32_t)(j0 + BK <= hi1));
         if (__builtin_amdgcn_ballot_w64(lane_full == 0u) == 0) return;

@@ -16,19 +16,26 @@ constexpr int kThreads = 256;
 constexpr int kLanesPerRow = 4;
 
 __device__ __forceinline__ void row_intervals(const AttnCall& c, int64_t i, int32_t* lo, int32_t* hi) {
-    if (!c.moba.enabled) {
-        lo[0] = 0; hi[0] = c.kv_total; lo[1] = 0; hi[1] = 0;
+    lo[1] = 0; hi[1] = 0;
+    if (c.mask.mode == kMaskNone) {
+        lo[0] = 0; hi[0] = c.kv_total;
         return;
     }
-    const int32_t L = c.moba.part_len, cl = c.moba.chunk_len;
+    if (c.mask.mode == kMaskCross) {  // environment prompt + this chunk's local prompt
+        const int32_t ch = (int32_t)(i / c.mask.part_len);
+        lo[0] = 0; hi[0] = c.mask.env_len;
+        lo[1] = c.mask.env_len + ch * c.mask.chunk_len; hi[1] = lo[1] + c.mask.chunk_len;
+        return;
+    }
+    const int32_t L = c.mask.part_len, cl = c.mask.chunk_len;
     const int32_t part = (int32_t)(i / L), r = (int32_t)(i % L), k = r / cl;
     const int32_t e = min((k + 1) * cl, L);
     if (part == 0) {              // clean: block-causal over clean chunks
-        lo[0] = 0; hi[0] = e; lo[1] = 0; hi[1] = 0;
+        lo[0] = 0; hi[0] = e;
     } else if (part == 1) {       // noisy: earlier clean chunks + its own noisy chunk
         lo[0] = 0; hi[0] = k * cl; lo[1] = L + k * cl; hi[1] = L + e;
     } else {                      // appended bidirectional block: itself only
-        lo[0] = 2 * L; hi[0] = 3 * L; lo[1] = 0; hi[1] = 0;
+        lo[0] = 2 * L; hi[0] = 3 * L;
     }
 }
 

@@ -177,7 +177,7 @@ void plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws
 }
 
 // Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
-int32_t moba_qtile_cost(const wmk::MobaShape& m, int32_t q_tokens, int32_t qt) {
+int32_t moba_qtile_cost(const wmk::MaskShape& m, int32_t q_tokens, int32_t qt) {
     const int32_t bq = wmk::attn_bf16_block_q();
     const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, q_tokens);
     const int32_t L = m.part_len, cl = m.chunk_len;
@@ -214,7 +214,7 @@ int32_t moba_qtile_cost(const wmk::MobaShape& m, int32_t q_tokens, int32_t qt) {
 // Longest-first launch order for MoBA: runs of consecutive q-tiles with equal
 // cost, sorted by decreasing cost.  Falls back to the natural order when there
 // are more runs than the kernel's table holds.
-void plan_moba_groups(wmk::AttnPlan& p, const wmk::MobaShape& m, int32_t q_tokens) {
+void plan_moba_groups(wmk::AttnPlan& p, const wmk::MaskShape& m, int32_t q_tokens) {
     struct Run { int32_t start, count, cost; };
     std::vector<Run> runs;
     for (int32_t qt = 0; qt < p.n_qtiles; ++qt) {
@@ -234,14 +234,14 @@ void plan_moba_groups(wmk::AttnPlan& p, const wmk::MobaShape& m, int32_t q_token
     p.n_groups = (int32_t)runs.size();
 }
 
-wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, bool moba, void* ws, size_t ws_bytes,
+wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
     if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
     hipError_t e;
     if (dtype == WMK_F32) {
         if (dry_run_path() != nullptr) {
-            dry_log("attn dtype=f32 q=%d heads=%d d=%d kv=%d moba=%d\n", call.q_tokens, call.heads, call.head_dim,
-                    call.kv_total, call.moba.enabled);
+            dry_log("attn dtype=f32 q=%d heads=%d d=%d kv=%d mask=%d\n", call.q_tokens, call.heads, call.head_dim,
+                    call.kv_total, call.mask.mode);
             return ok();
         }
         e = wmk::launch_attn_f32(call, stream);
@@ -252,17 +252,23 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, bool moba, 
         p.n_qtiles = (call.q_tokens + bq - 1) / bq;
         p.n_units = p.n_qtiles * call.heads;
         p.splits = 1;
-        if (moba) {
-            plan_moba_groups(p, call.moba, call.q_tokens);
+        if (call.mask.mode == wmk::kMaskMoba) {
+            plan_moba_groups(p, call.mask, call.q_tokens);
             p.xcd_remap = 0;
         } else {
+            // every q-tile visits the same number of key tiles: the whole key
+            // range, or (cross mask) the environment prompt plus its chunks'
+            // local prompts
+            int32_t tiles = (call.kv_total + kBK - 1) / kBK;
+            if (call.mask.mode == wmk::kMaskCross)
+                tiles = (call.mask.env_len + kBK - 1) / kBK + (call.mask.chunk_len + kBK - 1) / kBK;
             p.xcd_remap = 1;
-            plan_split(p, call.head_dim, (call.kv_total + kBK - 1) / kBK, ws, ws_bytes);
+            plan_split(p, call.head_dim, tiles, ws, ws_bytes);
         }
         if (dry_run_path() != nullptr) {
-            dry_log("attn dtype=bf16 q=%d heads=%d d=%d kv=%d moba=%d bq=%d units=%d qtiles=%d groups=%d "
+            dry_log("attn dtype=bf16 q=%d heads=%d d=%d kv=%d mask=%d bq=%d units=%d qtiles=%d groups=%d "
                     "split_units=%d splits=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total,
-                    call.moba.enabled, bq, p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
+                    call.mask.mode, bq, p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
             for (int g = 0; g < p.n_groups; ++g) dry_log("group %d %d\n", p.grp_start[g], p.grp_count[g]);
             return ok();
         }
@@ -452,8 +458,8 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
     call.head_dim = hd->head_dim;
     call.kv_total = (int32_t)total;
     call.scale = scale;
-    call.moba.enabled = 0;
-    return run_attention(call, hd->dtype, false, workspace, workspace_bytes, stream);
+    call.mask.mode = wmk::kMaskNone;
+    return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
 }
 
 wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
@@ -486,13 +492,52 @@ wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, c
     call.head_dim = hd->head_dim;
     call.kv_total = (int32_t)total;
     call.scale = scale;
-    call.moba.enabled = 1;
-    call.moba.part_len = (int32_t)L;
-    call.moba.chunk_len = std::min(m->chunk_frames, m->frames) * m->tokens_per_frame;
-    call.moba.parts = 2 + m->bidir_block;
-    (void)workspace;
+    call.mask.mode = wmk::kMaskMoba;
+    call.mask.part_len = (int32_t)L;
+    call.mask.chunk_len = std::min(m->chunk_frames, m->frames) * m->tokens_per_frame;
+    call.mask.parts = 2 + m->bidir_block;
+    (void)workspace;  // MoBA q-tiles differ in cost: longest first, no split tail
     (void)workspace_bytes;
-    return run_attention(call, hd->dtype, true, nullptr, 0, stream);
+    return run_attention(call, hd->dtype, nullptr, 0, stream);
+}
+
+wmk_status wmk_cross_attention_train(const wmk_xattn_desc* x, const wmk_head_desc* hd, const void* q, const void* k,
+                                     const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+    if (x == nullptr) return fail(WMK_ERR_NULL, "cross-attention descriptor is NULL");
+    wmk_status s = check_head(hd);
+    if (s != WMK_OK) return s;
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return fail(WMK_ERR_NULL, "q, k, v and out must not be NULL");
+    if (x->chunk_q_tokens < 1 || x->chunks < 1 || x->env_tokens < 0 || x->local_tokens < 0 ||
+        x->env_tokens + (int64_t)x->local_tokens < 1)
+        return fail(WMK_ERR_SHAPE, "cross-attention descriptor: chunk_q_tokens %d chunks %d env %d local %d",
+                    x->chunk_q_tokens, x->chunks, x->env_tokens, x->local_tokens);
+    const int64_t nq = (int64_t)x->chunk_q_tokens * x->chunks;
+    const int64_t nk = x->env_tokens + (int64_t)x->local_tokens * x->chunks;
+    if (nq > INT32_MAX || nk > INT32_MAX) return fail(WMK_ERR_SHAPE, "more than 2^31 - 1 query or key tokens");
+    if ((s = check_scale(scale)) != WMK_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(WMK_ERR_ALIGN, "q/k/v/out must be 16-byte aligned");
+    wmk::AttnCall call;
+    memset(&call, 0, sizeof call);
+    call.kv.k[0] = k;
+    call.kv.v[0] = v;
+    call.kv.end[0] = (int32_t)nk;
+    call.kv.n = 1;
+    call.q = q;
+    call.out = out;
+    call.q_tokens = (int32_t)nq;
+    call.heads = hd->num_heads;
+    call.head_dim = hd->head_dim;
+    call.kv_total = (int32_t)nk;
+    call.scale = scale;
+    call.mask.mode = wmk::kMaskCross;
+    call.mask.part_len = x->chunk_q_tokens;
+    call.mask.chunk_len = x->local_tokens;
+    call.mask.parts = x->chunks;
+    call.mask.env_len = x->env_tokens;
+    return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
 }
 
 const char* wmk_last_error(void) { return g_err.c_str(); }

@@ -22,12 +22,25 @@ struct KvSpans {
     int32_t n;
 };
 
-// The MoBA sequence [clean | noisy | block]; parts = 2 or 3.
-struct MobaShape {
-    int32_t enabled;
-    int32_t part_len;   // frames * tokens_per_frame
-    int32_t chunk_len;  // chunk_frames * tokens_per_frame
+// Per-row key mask of an attention call (every row allows at most two
+// half-open key ranges):
+//   kMaskNone:  every key (chunk attention at a denoising step);
+//   kMaskMoba:  the MoBA training sequence [clean | noisy | block]: part_len =
+//               frames * tokens_per_frame, chunk_len = chunk_frames *
+//               tokens_per_frame, parts = 2 or 3;
+//   kMaskCross: chunk-causal cross-attention over a multi-chunk sequence: query
+//               chunk i (part_len rows each, parts chunks) reads the env_len
+//               environment-prompt keys and local prompt i (chunk_len keys at
+//               env_len + i * chunk_len) only.
+constexpr int32_t kMaskNone = 0;
+constexpr int32_t kMaskMoba = 1;
+constexpr int32_t kMaskCross = 2;
+struct MaskShape {
+    int32_t mode;
+    int32_t part_len;
+    int32_t chunk_len;
     int32_t parts;
+    int32_t env_len;
 };
 
 struct AttnCall {
@@ -39,7 +52,7 @@ struct AttnCall {
     int32_t kv_total;
     float scale;
     KvSpans kv;
-    MobaShape moba;
+    MaskShape mask;
 };
 
 // Work plan for the bf16 MFMA kernel: which (head, q-tile) units run in which

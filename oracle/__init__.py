@@ -24,7 +24,9 @@ Sources (cited by page title and section):
   World Models", Overview, "Mix the training modes" and "Condition each chunk":
   chunks are generated from current inputs and cached history; MoBA mixes
   teacher forcing with bidirectional training; each chunk's cross-attention
-  reads the shared environment prompt and its own local prompt only.
+  reads the shared environment prompt and its own local prompt only (at
+  inference one chunk at a time; in training every chunk of a sequence at
+  once, under the causal cross-attention mask).
 
 Readings where the pages are silent (all stated once more in the design notes):
 sinks and window are counted in latent frames; the window excludes the current
@@ -302,3 +304,18 @@ def cross_attention(q, chunk, k_env, v_env, k_locals, v_locals, scale, rows=None
         q = q[np.asarray(rows)]
     iv = cross_row_intervals(chunk, k_env.shape[0], k_locals[0].shape[0])
     return attend(q, k_all, v_all, [iv] * q.shape[0], scale)
+
+
+def cross_train_row_intervals(i, chunk_q_tokens, env_tokens, local_tokens):
+    """Training form over a multi-chunk sequence: query row i belongs to chunk
+    i // chunk_q_tokens and reads the environment prompt and that chunk's local
+    prompt only, over keys [env | local_0 | local_1 | ...]."""
+    return cross_row_intervals(i // chunk_q_tokens, env_tokens, local_tokens)
+
+
+def cross_attention_train(q, k, v, chunk_q_tokens, env_tokens, local_tokens, scale, rows=None):
+    """Chunk-causal cross-attention of every query chunk at once; fp64 rows."""
+    q = np.asarray(q)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    ivs = [cross_train_row_intervals(int(i), chunk_q_tokens, env_tokens, local_tokens) for i in rows]
+    return attend(q[rows], k, v, ivs, scale)

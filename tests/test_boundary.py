@@ -301,3 +301,45 @@ def test_moba_argument_errors(lib, dry):
         wmk.WMK_ERR_NULL
     assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.0, None, 0, None) \
         == wmk.WMK_ERR_RANGE
+
+
+def test_cross_train_argument_errors_and_plan(lib, dry):
+    """Chunk-causal cross-attention over a multi-chunk sequence: bad descriptors are
+    refused before anything is planned; a valid call plans the cross mask over
+    q = chunks * chunk_q_tokens rows and env + chunks * local keys, and splits the
+    last round when workspace is given (every q-tile visits the same key tiles)."""
+    hd = wmk.wmk_head_desc(24, 128, wmk.WMK_BF16)
+    bad = [(wmk.wmk_xattn_desc(0, 4, 512, 512), wmk.WMK_ERR_SHAPE),
+           (wmk.wmk_xattn_desc(14400, 0, 512, 512), wmk.WMK_ERR_SHAPE),
+           (wmk.wmk_xattn_desc(14400, 4, -1, 512), wmk.WMK_ERR_SHAPE),
+           (wmk.wmk_xattn_desc(14400, 4, 512, -1), wmk.WMK_ERR_SHAPE),
+           (wmk.wmk_xattn_desc(14400, 4, 0, 0), wmk.WMK_ERR_SHAPE),
+           (wmk.wmk_xattn_desc(1 << 20, 1 << 12, 512, 512), wmk.WMK_ERR_SHAPE)]
+    for xd, status in bad:
+        n_before = len(dry.read_text().splitlines()) if dry.exists() else 0
+        assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088,
+                                             None, 0, None) == status
+        assert (len(dry.read_text().splitlines()) if dry.exists() else 0) == n_before
+    xd = wmk.wmk_xattn_desc(14400, 4, 512, 512)
+    assert lib.wmk_cross_attention_train(None, ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.1, None, 0, None) == \
+        wmk.WMK_ERR_NULL
+    assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, 0, OBUF, 0.1, None, 0,
+                                         None) == wmk.WMK_ERR_NULL
+    assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF + 4, KBUF, VBUF, OBUF, 0.1, None,
+                                         0, None) == wmk.WMK_ERR_ALIGN
+    assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, -1.0, None, 0,
+                                         None) == wmk.WMK_ERR_RANGE
+    assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088, None, 0,
+                                         None) == wmk.WMK_OK
+    p = _last_attn(dry)
+    bq = int(p["bq"])
+    qtiles = (4 * 14400 + bq - 1) // bq
+    assert (p["mask"], p["q"], p["kv"], p["qtiles"], p["units"], p["split_units"]) == \
+        ("2", str(4 * 14400), str(512 + 4 * 512), str(qtiles), str(24 * qtiles), "0")
+    wsb = lib.wmk_attention_workspace_bytes(ctypes.byref(hd), 4 * 14400)
+    assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088,
+                                         0x60000000, wsb, None) == wmk.WMK_OK
+    p = _last_attn(dry)
+    tail = (24 * qtiles) % 256
+    # 8 + 8 key tiles per q-tile: exactly two pieces of the minimum size
+    assert int(p["split_units"]) == tail and int(p["splits"]) == min(256 // tail, 16 // 8)

@@ -466,6 +466,76 @@ def test_cross_attention_ignores_other_chunks_prompts():
     np.testing.assert_allclose(a, ref, atol=1e-12)
 
 
+def _xtrain_case(seed, cq=3, nc=4, ne=2, nl=3, H=2, D=16):
+    q = _rand((cq * nc, H, D), seed)
+    k = _rand((ne + nc * nl, H, D), seed + 1)
+    v = _rand((ne + nc * nl, H, D), seed + 2)
+    return q, k, v
+
+
+def test_cross_train_zero_query_gives_mean_of_env_and_own_prompt():
+    """Closed form (C1) per chunk: q = 0 gives the plain mean of the values of
+    the environment prompt and of the chunk's own local prompt."""
+    cq, nc, ne, nl = 3, 4, 2, 3
+    _, k, v = _xtrain_case(300, cq, nc, ne, nl)
+    q = np.zeros((cq * nc,) + k.shape[1:], np.float32)
+    out = oracle.cross_attention_train(q, k, v, cq, ne, nl, 0.3)
+    for c in range(nc):
+        allowed = np.concatenate([v[:ne], v[ne + c * nl: ne + (c + 1) * nl]]).astype(np.float64)
+        for r in range(c * cq, (c + 1) * cq):
+            np.testing.assert_allclose(out[r], allowed.mean(axis=0), atol=1e-12)
+
+
+def test_cross_train_without_env_is_plain_attention_per_chunk():
+    """No environment prompt: chunk c is textbook softmax attention of its
+    queries over its own local prompt alone."""
+    cq, nc, ne, nl, H, D = 3, 4, 0, 5, 2, 16
+    q, k, v = _xtrain_case(310, cq, nc, ne, nl, H, D)
+    out = oracle.cross_attention_train(q, k, v, cq, ne, nl, 0.25)
+    for c in range(nc):
+        for h in range(H):
+            qc = q[c * cq:(c + 1) * cq, h].astype(np.float64)
+            kc = k[c * nl:(c + 1) * nl, h].astype(np.float64)
+            vc = v[c * nl:(c + 1) * nl, h].astype(np.float64)
+            logits = 0.25 * qc @ kc.T
+            p = np.exp(logits - logits.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            np.testing.assert_allclose(out[c * cq:(c + 1) * cq, h], p @ vc, atol=1e-12)
+
+
+def test_cross_train_one_chunk_is_full_attention():
+    """A single chunk reads every key: plain dense attention."""
+    cq, ne, nl = 5, 4, 3
+    q, k, v = _xtrain_case(320, cq, 1, ne, nl)
+    out = oracle.cross_attention_train(q, k, v, cq, ne, nl, 0.3)
+    ref, _ = dense_masked_softmax(q, k, v, np.ones((cq, ne + nl), bool), 0.3)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+
+
+def test_cross_train_chunks_ignore_other_prompts_and_match_inference_form():
+    """I9 in the training form: altering local prompt j changes only chunk j's
+    rows; chunk c's rows equal the inference call of chunk c."""
+    cq, nc, ne, nl, H, D = 3, 4, 2, 3, 2, 16
+    q, k, v = _xtrain_case(330, cq, nc, ne, nl, H, D)
+    a = oracle.cross_attention_train(q, k, v, cq, ne, nl, 0.25)
+    for j in range(nc):
+        k2, v2 = k.copy(), v.copy()
+        k2[ne + j * nl: ne + (j + 1) * nl] *= -2
+        v2[ne + j * nl: ne + (j + 1) * nl] += 1
+        b = oracle.cross_attention_train(q, k2, v2, cq, ne, nl, 0.25)
+        for c in range(nc):
+            rows = slice(c * cq, (c + 1) * cq)
+            if c == j:
+                assert np.abs(a[rows] - b[rows]).max() > 1e-3
+            else:
+                np.testing.assert_array_equal(a[rows], b[rows])
+    kl = [k[ne + c * nl: ne + (c + 1) * nl] for c in range(nc)]
+    vl = [v[ne + c * nl: ne + (c + 1) * nl] for c in range(nc)]
+    for c in range(nc):
+        inf = oracle.cross_attention(q[c * cq:(c + 1) * cq], c, k[:ne], v[:ne], kl, vl, 0.25)
+        np.testing.assert_allclose(a[c * cq:(c + 1) * cq], inf, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------------------------
 # input generator
 # ---------------------------------------------------------------------------------------------
