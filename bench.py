@@ -270,6 +270,45 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps):
     del c, q, k, v, o
     torch.cuda.empty_cache()
 
+    # rolling session at 832x464: 30 layers x 4 denoising steps per chunk over a
+    # full 18-slot cache, then the finalized chunk appended to every layer
+    layers, steps = 30, 4
+    nq = CF * TPF
+    rc = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
+                   window_frames=W, chunk_frames=CF)
+    pool = [tuple(fill((nq, H, D), chunk=i, kind=t) for t in (synth.Q, synth.K, synth.V)) for i in range(2)]
+    fin = [tuple(fill((nq, H, D), chunk=i, step=4, kind=t) for t in (synth.KFIN, synth.VFIN)) for i in range(2)]
+    ro = torch.empty((nq, H, D), dtype=torch.bfloat16, device=dev)
+
+    def chunk(ci):
+        for st in range(steps):
+            for l in range(layers):
+                rq, rk, rv = pool[(st + l) % 2]
+                wmk.chunk_attention(rc, l, rq, [(rk, rv)], out=ro)
+        for l in range(layers):
+            rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
+
+    for ci in range(4):  # warm the cache to 14 resident frames
+        for l in range(layers):
+            rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
+    chunk(4)
+    torch.cuda.synchronize()
+    n_chunks = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for ci in range(n_chunks):
+        chunk(5 + ci)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_chunk = e0.elapsed_time(e1) / n_chunks
+    chunk_flops = layers * steps * 4.0 * D * H * nq * (S + W + CF) * TPF
+    res["rolling_832x464_steady_chunk"] = {
+        "ms_per_chunk": round(per_chunk, 2), "calls_per_chunk": layers * steps, "appends_per_chunk": layers,
+        "tflops": round(chunk_flops / per_chunk / 1e9, 1),
+        "ms_per_60_chunk_session_at_steady_rate": round(60 * per_chunk, 1)}
+    del rc, pool, fin, ro
+    torch.cuda.empty_cache()
+
     # chunk-causal cross-attention over a training sequence: the MoBA shape's 7
     # chunks of 3 frames x 1560 tokens, each reading a 512-token environment
     # prompt and its own 512-token local prompt (12 heads)
