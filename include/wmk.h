@@ -170,6 +170,27 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
                                int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Chunk attention with variable retention: as wmk_chunk_attention, but of
+ * the resident frames of `layer` only the n_keep listed in keep_frames (a
+ * host array of global frame indices, any order, as reported by
+ * wmk_cache_slots) are attended; the others stay in the cache, untouched, for
+ * later calls.  This is the per-call choice of retained history of a dynamic
+ * KV-cache scheduler ("LingBot-World-Infinity" overview, deployment: retained
+ * history adapted to the current control signal).  Temporary auxiliary KV
+ * blocks of the current chunk ("World in World", second paragraph: extra
+ * evidence for the current chunk, dropped once it is finalized) are passed as
+ * segments and never appended.  n_keep = 0 attends the segments only.  The
+ * kept frames form one key span per run of adjacent slots; together with the
+ * segments at most 16 spans.
+ * Errors: c NULL, or keep_frames NULL with n_keep > 0 -> WMK_ERR_NULL;
+ * n_keep < 0 -> WMK_ERR_SHAPE; a listed frame not resident in the layer, or
+ * listed twice -> WMK_ERR_RANGE; more than 16 spans -> WMK_ERR_CAPACITY; the
+ * rest as for wmk_chunk_attention.  Nothing is enqueued on error. */
+wmk_status wmk_chunk_attention_retained(const wmk_cache* c, int32_t layer, const int64_t* keep_frames,
+                                        int32_t n_keep, const wmk_head_desc* hd, const void* q, int32_t q_tokens,
+                                        const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* MoBA-masked attention forward over one training sequence
  * [clean | noisy | block] ("Infinite Worlds with Versatile Interactions",
  * causal pretraining paragraph; "Mix Forcing", "Mix the training modes").

@@ -61,6 +61,10 @@ _SIGNATURES = {
     "wmk_chunk_attention": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
                                            ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P, ctypes.c_float, _P,
                                            ctypes.c_size_t, _P]),
+    "wmk_chunk_attention_retained": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                                    ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
+                                                    ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P,
+                                                    ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "wmk_moba_attention": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P, _P, _P,
                                           _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "wmk_cross_attention_train": (ctypes.c_int, [ctypes.POINTER(wmk_xattn_desc), ctypes.POINTER(wmk_head_desc), _P,
@@ -201,9 +205,12 @@ class Cache:
             pass
 
 
-def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_workspace=True, stream=None):
+def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_workspace=True, stream=None,
+                    keep_frames=None):
     """out[q_tokens][H][D] = attention of q over the resident frames of `layer` in `cache`
-    (None for none) and every token of `segments` (a list of (k, v) tensors)."""
+    (None for none) and every token of `segments` (a list of (k, v) tensors).
+    keep_frames: attend only these resident frames (global frame indices);
+    None attends all of them."""
     torch = _torch()
     nq, H, D = q.shape
     if out is None:
@@ -219,8 +226,16 @@ def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_work
         if wsb:
             w = workspace(q.device, wsb)
             ws, wsb = _ptr(w), w.numel()
-    _check(load().wmk_chunk_attention(cache.handle if cache is not None else None, layer, ctypes.byref(hd), _ptr(q),
-                                      nq, segs, len(segments), _ptr(out), scale, ws, wsb, _stream_ptr(stream)))
+    if keep_frames is None:
+        _check(load().wmk_chunk_attention(cache.handle if cache is not None else None, layer, ctypes.byref(hd),
+                                          _ptr(q), nq, segs, len(segments), _ptr(out), scale, ws, wsb,
+                                          _stream_ptr(stream)))
+    else:
+        keep = [int(f) for f in keep_frames]
+        arr = (ctypes.c_int64 * max(1, len(keep)))(*keep)
+        _check(load().wmk_chunk_attention_retained(cache.handle if cache is not None else None, layer, arr,
+                                                   len(keep), ctypes.byref(hd), _ptr(q), nq, segs, len(segments),
+                                                   _ptr(out), scale, ws, wsb, _stream_ptr(stream)))
     return out
 
 

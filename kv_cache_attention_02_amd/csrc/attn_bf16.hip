@@ -95,8 +95,9 @@ __device__ __forceinline__ int swz_k(int row) { return row & 15 & (Cfg<D>::CPR -
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return (((row & 3) << 2) | ((row >> 2) & 1)) & (Cfg<D>::CPR - 1); }
 
+template <int NS>
 struct Params {
-    AttnCall c;
+    AttnCallN<NS> c;
     AttnPlan p;
 };
 
@@ -132,7 +133,8 @@ __device__ __forceinline__ void emit(TileRanges& r, int k, int32_t b, int32_t e)
     r.b3 = k == 3 ? b : r.b3; r.e3 = k == 3 ? e : r.e3;
 }
 
-__device__ __forceinline__ TileRanges tile_ranges(const AttnCall& c, int32_t r0, int32_t r1) {
+template <class Call>
+__device__ __forceinline__ TileRanges tile_ranges(const Call& c, int32_t r0, int32_t r1) {
     int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
     if (c.mask.mode == kMaskNone) {
         set_tiles(l0, h0, 0, c.kv_total);
@@ -195,7 +197,8 @@ __device__ __forceinline__ int32_t range_end_at(const TileRanges& r, int32_t it)
 }
 
 // Allowed key ranges of one query row (see wmk.h).
-__device__ __forceinline__ void row_ranges(const AttnCall& c, int32_t row, int32_t& lo0, int32_t& hi0, int32_t& lo1,
+template <class Call>
+__device__ __forceinline__ void row_ranges(const Call& c, int32_t row, int32_t& lo0, int32_t& hi0, int32_t& lo1,
                                            int32_t& hi1) {
     lo1 = 0; hi1 = 0;
     if (c.mask.mode == kMaskNone || row >= c.q_tokens) { lo0 = 0; hi0 = c.kv_total; return; }
@@ -231,10 +234,11 @@ struct SpanSel {
     int32_t start, end;
 };
 
-__device__ __forceinline__ SpanSel span_sel(const KvSpans& kv, int32_t j) {
+template <int N>
+__device__ __forceinline__ SpanSel span_sel(const KvSpansN<N>& kv, int32_t j) {
     SpanSel r{(const char*)kv.k[0], (const char*)kv.v[0], 0, kv.end[0]};
 #pragma unroll
-    for (int x = 0; x < kMaxSeg - 1; ++x) {
+    for (int x = 0; x < N - 1; ++x) {
         const bool past = (x < kv.n - 1) && (j >= kv.end[x]);
         r.k = past ? (const char*)kv.k[x + 1] : r.k;
         r.v = past ? (const char*)kv.v[x + 1] : r.v;
@@ -257,7 +261,8 @@ struct Cursor {
     const char* v;
 };
 
-__device__ __forceinline__ Cursor cursor_at(const AttnCall& c, const TileRanges& tr, int32_t it, int64_t row_bytes,
+template <class Call>
+__device__ __forceinline__ Cursor cursor_at(const Call& c, const TileRanges& tr, int32_t it, int64_t row_bytes,
                                             int64_t head_off) {
     Cursor cu;
     cu.tile = tile_at(tr, it);
@@ -270,7 +275,8 @@ __device__ __forceinline__ Cursor cursor_at(const AttnCall& c, const TileRanges&
     return cu;
 }
 
-__device__ __forceinline__ void advance(Cursor& cu, const AttnCall& c, const TileRanges& tr, int32_t it_next,
+template <class Call>
+__device__ __forceinline__ void advance(Cursor& cu, const Call& c, const TileRanges& tr, int32_t it_next,
                                         int64_t row_bytes, int64_t head_off) {
     if (cu.run > 1) {
         cu.tile += 1;
@@ -344,8 +350,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, ch
 // span end (or the last key) loads each span's rows under a lane mask; rows
 // past the last key read the last key instead (finite data that the mask
 // drops).
-template <int D>
-__device__ __forceinline__ void issue_tile(const AttnCall& c, int32_t head, const Cursor& cu, const LoadMap<D>& m,
+template <int D, class Call>
+__device__ __forceinline__ void issue_tile(const Call& c, int32_t head, const Cursor& cu, const LoadMap<D>& m,
                                            int wave, const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
     using C = Cfg<D>;
     const int64_t row_bytes = (int64_t)c.heads * D * 2;
@@ -473,10 +479,10 @@ struct SplitWs {
     }
 };
 
-template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params prm) {
+template <int D, int NS>
+__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     using C = Cfg<D>;
-    const AttnCall& c = prm.c;
+    const AttnCallN<NS>& c = prm.c;
     const AttnPlan& p = prm.p;
     // Separate LDS objects, each named statically in the unrolled loop below
     // (buffer stage x part), so the compiler can tell the objects being filled
@@ -965,29 +971,49 @@ int attn_bf16_blocks_per_cu(int head_dim) {
     int n = 0;
     hipError_t e;
     if (head_dim == 64)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64>, NT, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kFewSeg>, NT, 0);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128>, NT, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, kFewSeg>, NT, 0);
     return (e == hipSuccess && n > 0) ? n : 1;
 }
 
-hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t s) {
-    Params prm;
-    prm.c = c;
+template <int NS>
+hipError_t launch_spans(const AttnCall& c, const AttnPlan& plan, int32_t blocks, hipStream_t s) {
+    Params<NS> prm;
+    prm.c.q = c.q;
+    prm.c.out = c.out;
+    prm.c.q_tokens = c.q_tokens;
+    prm.c.heads = c.heads;
+    prm.c.head_dim = c.head_dim;
+    prm.c.kv_total = c.kv_total;
+    prm.c.scale = c.scale;
+    prm.c.mask = c.mask;
+    for (int x = 0; x < NS; ++x) {
+        const bool in = x < c.kv.n;
+        prm.c.kv.k[x] = in ? c.kv.k[x] : nullptr;
+        prm.c.kv.v[x] = in ? c.kv.v[x] : nullptr;
+        prm.c.kv.end[x] = in ? c.kv.end[x] : c.kv_total;
+    }
+    prm.c.kv.n = c.kv.n;
     prm.p = plan;
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL((attn_bf16_kernel<64, NS>), dim3(blocks), dim3(NT), 0, s, prm);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NS>), dim3(blocks), dim3(NT), 0, s, prm);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t s) {
     const int32_t blocks = plan.n_units - plan.split_units + plan.split_units * plan.splits;
     if (blocks <= 0) return hipSuccess;
+    if (c.kv.n < 0 || c.kv.n > kMaxSeg || (c.head_dim != 64 && c.head_dim != 128)) return hipErrorInvalidValue;
     if (plan.split_units > 0) {
         hipLaunchKernelGGL(zero_ints, dim3((plan.split_units + 255) / 256), dim3(256), 0, s, (int*)plan.ws,
                            plan.split_units);
     }
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(blocks), dim3(NT), 0, s, prm);
-    else if (c.head_dim == 128)
-        hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(blocks), dim3(NT), 0, s, prm);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    // one cache run plus up to 4 segments (every call but a retained subset of
+    // scattered frames): a span table small enough to stay in scalar registers
+    return c.kv.n <= kFewSeg ? launch_spans<kFewSeg>(c, plan, blocks, s) : launch_spans<kMaxSeg>(c, plan, blocks, s);
 }
 
 }  // namespace wmk

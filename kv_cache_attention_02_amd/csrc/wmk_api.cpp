@@ -270,12 +270,103 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
                     "split_units=%d splits=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total,
                     call.mask.mode, bq, p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
             for (int g = 0; g < p.n_groups; ++g) dry_log("group %d %d\n", p.grp_start[g], p.grp_count[g]);
+            for (int x = 0; x < call.kv.n; ++x)
+                dry_log("span %d %d %llx %llx\n", x, call.kv.end[x], (unsigned long long)(uintptr_t)call.kv.k[x],
+                        (unsigned long long)(uintptr_t)call.kv.v[x]);
             return ok();
         }
         e = wmk::launch_attn_bf16(call, p, stream);
     }
     if (e != hipSuccess) return fail(WMK_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+const int64_t kNoFrame = -1;
+
+// Chunk attention over the resident frames of `layer` (keep == NULL: all of
+// them; else the n_keep listed frames) plus the caller's segments.  The cache
+// part becomes one span per run of adjacent selected slots, in slot order:
+// softmax does not depend on the order of the keys.
+wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t* keep, int32_t n_keep,
+                                const wmk_head_desc* hd, const void* q, int32_t q_tokens, const wmk_kv_segment* seg,
+                                int32_t n_seg, void* out, float scale, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+    wmk_status s = check_head(hd);
+    if (s != WMK_OK) return s;
+    if (q == nullptr || out == nullptr) return fail(WMK_ERR_NULL, "q and out must not be NULL");
+    if (n_seg < 0 || n_seg > wmk::kMaxCallerSeg)
+        return fail(WMK_ERR_SHAPE, "n_seg %d outside [0, %d]", n_seg, wmk::kMaxCallerSeg);
+    if (n_seg > 0 && seg == nullptr) return fail(WMK_ERR_NULL, "seg is NULL with n_seg %d", n_seg);
+    if (q_tokens <= 0) return fail(WMK_ERR_SHAPE, "q_tokens %d <= 0", q_tokens);
+    if ((s = check_scale(scale)) != WMK_OK) return s;
+    if (!aligned16(q) || !aligned16(out)) return fail(WMK_ERR_ALIGN, "q/out must be 16-byte aligned");
+    if (c != nullptr) {
+        if (layer < 0 || layer >= c->d.num_layers)
+            return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, c->d.num_layers);
+        if (c->d.num_heads != hd->num_heads || c->d.head_dim != hd->head_dim)
+            return fail(WMK_ERR_SHAPE, "head descriptor (%d x %d) does not match the cache (%d x %d)",
+                        hd->num_heads, hd->head_dim, c->d.num_heads, c->d.head_dim);
+        if (c->d.dtype != hd->dtype) return fail(WMK_ERR_DTYPE, "dtype differs from the cache's");
+    }
+    wmk::AttnCall call;
+    memset(&call, 0, sizeof call);
+    int64_t total = 0;
+    int n = 0;
+    if (c != nullptr) {
+        const wmk_cache_desc& d = c->d;
+        const int32_t slots = d.sink_frames + d.window_frames;
+        const int64_t F = c->frames[layer];
+        std::vector<char> sel(slots, 0);
+        if (keep == nullptr) {
+            std::fill(sel.begin(), sel.begin() + valid_of(d, F), 1);
+        } else {
+            for (int32_t i = 0; i < n_keep; ++i) {
+                const int64_t f = keep[i];
+                const bool resident = f >= 0 && f < F && (f < d.sink_frames || f >= std::max<int64_t>(d.sink_frames, F - d.window_frames));
+                if (!resident) return fail(WMK_ERR_RANGE, "frame %lld is not resident in layer %d", (long long)f, layer);
+                const int64_t slot = f < d.sink_frames ? f : d.sink_frames + (f - d.sink_frames) % d.window_frames;
+                if (sel[slot]) return fail(WMK_ERR_RANGE, "frame %lld listed twice", (long long)f);
+                sel[slot] = 1;
+            }
+        }
+        const size_t base = (size_t)layer * c->layer_bytes;
+        for (int32_t a = 0; a < slots;) {
+            if (!sel[a]) { ++a; continue; }
+            int32_t b = a;
+            while (b < slots && sel[b]) ++b;
+            if (n + n_seg >= wmk::kMaxSeg)
+                return fail(WMK_ERR_CAPACITY, "retained frames form more than %d runs of adjacent slots with %d segments",
+                            wmk::kMaxSeg - n_seg, n_seg);
+            call.kv.k[n] = c->k + base + (size_t)a * c->frame_bytes;
+            call.kv.v[n] = c->v + base + (size_t)a * c->frame_bytes;
+            total += (int64_t)(b - a) * d.tokens_per_frame;
+            call.kv.end[n] = (int32_t)total;  // < 2^31: the cache size check bounds a layer's tokens
+            ++n;
+            a = b;
+        }
+    }
+    for (int i = 0; i < n_seg; ++i) {
+        if (seg[i].k == nullptr || seg[i].v == nullptr) return fail(WMK_ERR_NULL, "segment %d has a NULL k/v", i);
+        if (seg[i].tokens <= 0) return fail(WMK_ERR_SHAPE, "segment %d has %d tokens", i, seg[i].tokens);
+        if (!aligned16(seg[i].k) || !aligned16(seg[i].v))
+            return fail(WMK_ERR_ALIGN, "segment %d k/v must be 16-byte aligned", i);
+        total += seg[i].tokens;
+        if (total > INT32_MAX) return fail(WMK_ERR_SHAPE, "more than 2^31 - 1 keys");
+        call.kv.k[n] = seg[i].k;
+        call.kv.v[n] = seg[i].v;
+        call.kv.end[n] = (int32_t)total;
+        ++n;
+    }
+    call.kv.n = n;
+    call.q = q;
+    call.out = out;
+    call.q_tokens = q_tokens;
+    call.heads = hd->num_heads;
+    call.head_dim = hd->head_dim;
+    call.kv_total = (int32_t)total;
+    call.scale = scale;
+    call.mask.mode = wmk::kMaskNone;
+    return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
 }
 
 }  // namespace
@@ -407,59 +498,19 @@ size_t wmk_attention_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens) 
 wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
                                int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    wmk_status s = check_head(hd);
-    if (s != WMK_OK) return s;
-    if (q == nullptr || out == nullptr) return fail(WMK_ERR_NULL, "q and out must not be NULL");
-    if (n_seg < 0 || n_seg > wmk::kMaxSeg - 1) return fail(WMK_ERR_SHAPE, "n_seg %d outside [0, 4]", n_seg);
-    if (n_seg > 0 && seg == nullptr) return fail(WMK_ERR_NULL, "seg is NULL with n_seg %d", n_seg);
-    if (q_tokens <= 0) return fail(WMK_ERR_SHAPE, "q_tokens %d <= 0", q_tokens);
-    if ((s = check_scale(scale)) != WMK_OK) return s;
-    if (!aligned16(q) || !aligned16(out)) return fail(WMK_ERR_ALIGN, "q/out must be 16-byte aligned");
-    if (c != nullptr) {
-        if (layer < 0 || layer >= c->d.num_layers)
-            return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, c->d.num_layers);
-        if (c->d.num_heads != hd->num_heads || c->d.head_dim != hd->head_dim)
-            return fail(WMK_ERR_SHAPE, "head descriptor (%d x %d) does not match the cache (%d x %d)",
-                        hd->num_heads, hd->head_dim, c->d.num_heads, c->d.head_dim);
-        if (c->d.dtype != hd->dtype) return fail(WMK_ERR_DTYPE, "dtype differs from the cache's");
-    }
-    wmk::AttnCall call;
-    memset(&call, 0, sizeof call);
-    int64_t total = 0;
-    int n = 0;
-    if (c != nullptr) {
-        const int64_t valid = valid_of(c->d, c->frames[layer]);
-        if (valid > 0) {
-            const size_t base = (size_t)layer * c->layer_bytes;
-            call.kv.k[n] = c->k + base;
-            call.kv.v[n] = c->v + base;
-            total += valid * c->d.tokens_per_frame;
-            call.kv.end[n] = (int32_t)total;
-            ++n;
-        }
-    }
-    for (int i = 0; i < n_seg; ++i) {
-        if (seg[i].k == nullptr || seg[i].v == nullptr) return fail(WMK_ERR_NULL, "segment %d has a NULL k/v", i);
-        if (seg[i].tokens <= 0) return fail(WMK_ERR_SHAPE, "segment %d has %d tokens", i, seg[i].tokens);
-        if (!aligned16(seg[i].k) || !aligned16(seg[i].v))
-            return fail(WMK_ERR_ALIGN, "segment %d k/v must be 16-byte aligned", i);
-        total += seg[i].tokens;
-        if (total > INT32_MAX) return fail(WMK_ERR_SHAPE, "more than 2^31 - 1 keys");
-        call.kv.k[n] = seg[i].k;
-        call.kv.v[n] = seg[i].v;
-        call.kv.end[n] = (int32_t)total;
-        ++n;
-    }
-    call.kv.n = n;
-    call.q = q;
-    call.out = out;
-    call.q_tokens = q_tokens;
-    call.heads = hd->num_heads;
-    call.head_dim = hd->head_dim;
-    call.kv_total = (int32_t)total;
-    call.scale = scale;
-    call.mask.mode = wmk::kMaskNone;
-    return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
+    return chunk_attention_impl(c, layer, nullptr, 0, hd, q, q_tokens, seg, n_seg, out, scale, workspace,
+                                workspace_bytes, stream);
+}
+
+wmk_status wmk_chunk_attention_retained(const wmk_cache* c, int32_t layer, const int64_t* keep_frames,
+                                        int32_t n_keep, const wmk_head_desc* hd, const void* q, int32_t q_tokens,
+                                        const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (c == nullptr) return fail(WMK_ERR_NULL, "retained attention needs a cache");
+    if (n_keep < 0) return fail(WMK_ERR_SHAPE, "n_keep %d < 0", n_keep);
+    if (n_keep > 0 && keep_frames == nullptr) return fail(WMK_ERR_NULL, "keep_frames is NULL with n_keep %d", n_keep);
+    return chunk_attention_impl(c, layer, keep_frames == nullptr ? &kNoFrame : keep_frames, n_keep, hd, q, q_tokens,
+                                seg, n_seg, out, scale, workspace, workspace_bytes, stream);
 }
 
 wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,

@@ -7,20 +7,24 @@
 
 namespace wmk {
 
-constexpr int kMaxSeg = 5;        // cache prefix + up to 4 caller segments
+constexpr int kMaxSeg = 16;       // spans of one call: cache runs + caller segments
+constexpr int kMaxCallerSeg = 4;  // caller segments of one call
+constexpr int kFewSeg = 5;        // span count of the common kernel (one cache run + 4 segments)
 constexpr int kMaxGroups = 64;    // q-tile groups of a longest-first launch order
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kMaxHeads = 4096;   // a 64-key tile of all heads stays below 2^31 bytes (32-bit buffer offsets)
 
 // Keys/values seen by one attention call: the virtual concatenation of up to
-// kMaxSeg spans, each [tokens][heads][head_dim].  seg_end is the exclusive
-// prefix sum of the span lengths.
-struct KvSpans {
-    const void* k[kMaxSeg];
-    const void* v[kMaxSeg];
-    int32_t end[kMaxSeg];
+// N spans, each [tokens][heads][head_dim].  end is the exclusive prefix sum of
+// the span lengths.
+template <int N>
+struct KvSpansN {
+    const void* k[N];
+    const void* v[N];
+    int32_t end[N];
     int32_t n;
 };
+using KvSpans = KvSpansN<kMaxSeg>;
 
 // Per-row key mask of an attention call (every row allows at most two
 // half-open key ranges):
@@ -43,7 +47,8 @@ struct MaskShape {
     int32_t env_len;
 };
 
-struct AttnCall {
+template <int N>
+struct AttnCallN {
     const void* q;
     void* out;
     int32_t q_tokens;
@@ -51,9 +56,10 @@ struct AttnCall {
     int32_t head_dim;
     int32_t kv_total;
     float scale;
-    KvSpans kv;
+    KvSpansN<N> kv;
     MaskShape mask;
 };
+using AttnCall = AttnCallN<kMaxSeg>;
 
 // Work plan for the bf16 MFMA kernel: which (head, q-tile) units run in which
 // launch order, and how the last partial round is split over the key range.

@@ -28,6 +28,10 @@ Sources (cited by page title and section):
   inference one chunk at a time; in training every chunk of a sequence at
   once, under the causal cross-attention mask).
 
+* "LingBot-World-Infinity" overview, deployment: a dynamic KV-cache scheduler
+  adapts the retained history to the current control signal (here: a call
+  attends a chosen subset of the resident frames).
+
 Readings where the pages are silent (all stated once more in the design notes):
 sinks and window are counted in latent frames; the window excludes the current
 chunk; append and evict happen in one call after a chunk is finalized; an
@@ -208,9 +212,18 @@ class CacheModel:
             kb[s], vb[s] = self.frames[f]
         return kb, vb
 
-    def logical_kv(self):
-        """Resident K and V concatenated in time order, [n_resident*tpf][H][D]."""
+    def logical_kv(self, frames=None):
+        """Resident K and V concatenated in time order, [n_resident*tpf][H][D].
+        ``frames``: only these resident frames (variable retention)."""
         fs = self.resident()
+        if frames is not None:
+            frames = [int(f) for f in frames]
+            if len(set(frames)) != len(frames):
+                raise ValueError("a retained frame is listed twice")
+            missing = set(frames) - set(fs)
+            if missing:
+                raise ValueError(f"frames {sorted(missing)} are not resident")
+            fs = sorted(frames)
         if not fs:
             e = np.zeros((0, self.H, self.D), dtype=self.dtype)
             return e, e.copy()
@@ -223,19 +236,27 @@ class CacheModel:
 # cached history; "World in World": anchors + recent + current chunk slots)
 # --------------------------------------------------------------------------------------------
 
-def chunk_attention(cache, q, segments, scale, rows=None):
+def chunk_attention(cache, q, segments, scale, rows=None, keep_frames=None):
     """Queries of the current chunk attend every resident cache frame and every
     token of the passed segments (the current chunk's own K/V, bidirectionally,
     or prompt K/V for cross-attention).  ``cache`` may be None.
 
     q: [nq][H][D]; segments: list of (k, v), each [n][H][D].  ``rows`` selects
     the query rows to evaluate (default: all).  Returns fp64 [len(rows)][H][D].
+
+    ``keep_frames``: variable retention ("LingBot-World-Infinity" overview,
+    deployment: a dynamic KV-cache scheduler adapts the retained history) --
+    only these resident frames are attended; the rest stay cached but unseen.
+    Temporary auxiliary KV blocks ("World in World", second paragraph) are
+    simply further segments.
     """
     ks, vs = [], []
     if cache is not None:
-        kc, vc = cache.logical_kv()
+        kc, vc = cache.logical_kv(keep_frames)
         ks.append(kc)
         vs.append(vc)
+    elif keep_frames:
+        raise ValueError("retained frames need a cache")
     for k, v in segments:
         ks.append(np.asarray(k))
         vs.append(np.asarray(v))

@@ -343,3 +343,100 @@ def test_cross_train_argument_errors_and_plan(lib, dry):
     tail = (24 * qtiles) % 256
     # 8 + 8 key tiles per q-tile: exactly two pieces of the minimum size
     assert int(p["split_units"]) == tail and int(p["splits"]) == min(256 // tail, 16 // 8)
+
+
+def _attn_keep(lib, h, layer, keep, hd, nq, segs, scale=0.088, keep_null=False):
+    arr = (wmk.wmk_kv_segment * max(1, len(segs)))(*[wmk.wmk_kv_segment(k, v, t) for k, v, t in segs])
+    ka = None if keep_null else (ctypes.c_int64 * max(1, len(keep)))(*keep)
+    return lib.wmk_chunk_attention_retained(h, layer, ka, len(keep), ctypes.byref(hd), QBUF, nq, arr, len(segs),
+                                            OBUF, scale, None, 0, None)
+
+
+def _spans(dry):
+    lines = dry.read_text().splitlines()
+    last = max(i for i, x in enumerate(lines) if x.startswith("attn"))
+    out = []
+    for x in lines[last + 1:]:
+        if x.startswith("span"):
+            _, _, end, k, v = x.split()
+            out.append((int(end), int(k, 16), int(v, 16)))
+    return out
+
+
+@pytest.mark.parametrize("S,W,cf,n_chunks,seed", [(6, 8, 4, 5, 0), (6, 8, 4, 3, 1), (2, 5, 3, 6, 2), (0, 7, 2, 9, 3)])
+def test_retained_spans_follow_slot_policy(lib, dry, S, W, cf, n_chunks, seed):
+    """Variable retention: the kept frames become one key span per run of adjacent
+    slots, at the slots the oracle's policy gives those frames, in slot order,
+    followed by the segments."""
+    tpf, H, D, L = 16, 2, 64, 3
+    d = _desc(L=L, H=H, D=D, tpf=tpf, S=S, W=W, cf=cf)
+    _, h = _init(lib, d)
+    cm = oracle.CacheModel(S, W, tpf, H, D)
+    for _ in range(n_chunks):
+        assert lib.wmk_cache_append_evict(h, 1, QBUF, SBUF, cf, None) == wmk.WMK_OK
+        cm.append(np.zeros((cf * tpf, H, D), np.uint16), np.zeros((cf * tpf, H, D), np.uint16), cf)
+    frame_b = tpf * H * D * 2
+    layer_b = (S + W) * frame_b
+    hd = wmk.wmk_head_desc(H, D, wmk.WMK_BF16)
+    rng = np.random.default_rng(seed)
+    res = cm.resident()
+    for trial in range(6):
+        keep = [int(f) for f in rng.permutation(res) if rng.random() < 0.5]
+        assert _attn_keep(lib, h, 1, keep, hd, 40, [(QBUF, SBUF, 40)]) == wmk.WMK_OK
+        slots = sorted(oracle.slot_of_frame(f, S, W) for f in keep)
+        runs = []
+        for s in slots:
+            if runs and runs[-1][1] == s:
+                runs[-1][1] = s + 1
+            else:
+                runs.append([s, s + 1])
+        want, end = [], 0
+        for a, b in runs:
+            end += (b - a) * tpf
+            want.append((end, KBUF + layer_b + a * frame_b, VBUF + layer_b + a * frame_b))
+        want.append((end + 40, QBUF, SBUF))
+        assert _spans(dry) == want, (keep, runs)
+        assert _last_attn(dry)["kv"] == str(end + 40)
+    # every resident frame: the same plan as plain chunk attention
+    assert _attn_keep(lib, h, 1, res, hd, 40, [(QBUF, SBUF, 40)]) == wmk.WMK_OK
+    a = _spans(dry)
+    assert _attn(lib, h, 1, hd, 40, [(QBUF, SBUF, 40)]) == wmk.WMK_OK
+    assert _spans(dry) == a
+    lib.wmk_cache_destroy(h)
+
+
+def test_retained_argument_errors(lib, dry):
+    S, W, tpf, H, D = 0, 40, 16, 2, 64
+    d = _desc(H=H, D=D, tpf=tpf, S=S, W=W, cf=40)
+    _, h = _init(lib, d)
+    assert lib.wmk_cache_append_evict(h, 0, QBUF, SBUF, 40, None) == wmk.WMK_OK   # frames 0..39 resident
+    hd = wmk.wmk_head_desc(H, D, wmk.WMK_BF16)
+    seg = [(QBUF, SBUF, 40)]
+    every_other = list(range(0, 40, 2))                      # 20 runs of one slot
+    bad = [
+        (dict(keep=[40]), wmk.WMK_ERR_RANGE), (dict(keep=[-1]), wmk.WMK_ERR_RANGE),
+        (dict(keep=[3, 3]), wmk.WMK_ERR_RANGE),
+        (dict(keep=[1], keep_null=True), wmk.WMK_ERR_NULL),
+        (dict(keep=every_other), wmk.WMK_ERR_CAPACITY),
+        (dict(keep=every_other[:13], segs=seg * 4), wmk.WMK_ERR_CAPACITY),
+        (dict(keep=[1], segs=seg * 5), wmk.WMK_ERR_SHAPE),
+        (dict(keep=[1], layer=1), wmk.WMK_ERR_RANGE),
+        (dict(keep=[1], scale=0.0), wmk.WMK_ERR_RANGE),
+    ]
+    for kw, status in bad:
+        args = dict(layer=0, keep=[], segs=seg, keep_null=False, scale=0.088)
+        args.update(kw)
+        n_before = len(dry.read_text().splitlines())
+        st = _attn_keep(lib, h, args["layer"], args["keep"], hd, 40, args["segs"], scale=args["scale"],
+                        keep_null=args["keep_null"])
+        assert st == status, (kw, st)
+        assert len(dry.read_text().splitlines()) == n_before
+    # a NULL cache is refused; 12 runs + 4 segments = 16 spans is the limit
+    arr = (wmk.wmk_kv_segment * 1)(wmk.wmk_kv_segment(QBUF, SBUF, 40))
+    assert lib.wmk_chunk_attention_retained(None, 0, None, 0, ctypes.byref(hd), QBUF, 40, arr, 1, OBUF, 0.1, None,
+                                            0, None) == wmk.WMK_ERR_NULL
+    assert _attn_keep(lib, h, 0, every_other[:12], hd, 40, seg * 4) == wmk.WMK_OK
+    assert len(_spans(dry)) == 16
+    assert _attn_keep(lib, h, 0, [], hd, 40, seg) == wmk.WMK_OK      # segments only
+    assert _spans(dry) == [(40, QBUF, SBUF)]
+    lib.wmk_cache_destroy(h)

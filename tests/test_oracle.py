@@ -344,6 +344,96 @@ def test_chunk_attention_rows_subset():
 
 
 # ---------------------------------------------------------------------------------------------
+# variable retention: a call attends a chosen subset of the resident frames
+# ---------------------------------------------------------------------------------------------
+
+def _retained_rollout(S, W, cf, tpf, H, D, n_chunks, seed, pick):
+    """Rollout where chunk c attends only pick(c, resident) of the resident frames."""
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    n = cf * tpf * H * D
+    qs, ks, vs, outs, kept = [], [], [], [], []
+    for c in range(n_chunks):
+        q = synth.normal(n, dtype="f32", seed=seed, chunk=c, kind=synth.Q).reshape(cf * tpf, H, D)
+        k = synth.normal(n, dtype="f32", seed=seed, chunk=c, kind=synth.K).reshape(cf * tpf, H, D)
+        v = synth.normal(n, dtype="f32", seed=seed, chunk=c, kind=synth.V).reshape(cf * tpf, H, D)
+        keep = pick(c, cm.resident())
+        kept.append(set(keep))
+        outs.append(oracle.chunk_attention(cm, q, [(k, v)], 1.0 / np.sqrt(D), keep_frames=keep))
+        cm.append(k, v, cf)
+        qs.append(q), ks.append(k), vs.append(v)
+    return np.concatenate(qs), np.concatenate(ks), np.concatenate(vs), np.concatenate(outs), kept
+
+
+@pytest.mark.parametrize("S,W,cf,policy", [(2, 4, 2, "random"), (1, 6, 3, "anchors_and_last"), (3, 3, 1, "random")])
+def test_retained_rollout_matches_dense_frame_mask(S, W, cf, policy):
+    """Retention stated pairwise: a query frame of chunk c sees its own chunk and exactly the
+    frames kept for chunk c, which must be a subset of the sinks and the last W frames."""
+    tpf, H, D, n = 3, 2, 8, 6
+    rng = np.random.default_rng(11)
+
+    def pick(c, resident):
+        if policy == "random":
+            return [f for f in resident if rng.random() < 0.6]
+        return [f for f in resident if f < S] + [f for f in resident if f >= S][-2:]   # anchors + 2 latest
+
+    q, k, v, out, kept = _retained_rollout(S, W, cf, tpf, H, D, n, seed=4, pick=pick)
+    fr = np.arange(n * cf * tpf) // tpf
+    mask = np.zeros((fr.size, fr.size), dtype=bool)
+    for a in range(fr.size):
+        c = fr[a] // cf
+        for b in range(fr.size):
+            mask[a, b] = (fr[b] // cf == c) or (fr[b] in kept[c] and rollout_allowed(fr[a], fr[b], S, W, cf))
+    ref, _ = dense_masked_softmax(q, k, v, mask, 1.0 / np.sqrt(D))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_retention_of_every_resident_frame_is_plain_chunk_attention():
+    S, W, cf, tpf, H, D = 2, 3, 2, 4, 2, 8
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    for c in range(4):
+        cm.append(_rand((cf * tpf, H, D), 70 + c), _rand((cf * tpf, H, D), 80 + c), cf)
+    q, k, v = _rand((cf * tpf, H, D), 90), _rand((cf * tpf, H, D), 91), _rand((cf * tpf, H, D), 92)
+    full = oracle.chunk_attention(cm, q, [(k, v)], 0.4)
+    shuffled = list(np.random.default_rng(2).permutation(cm.resident()))
+    np.testing.assert_array_equal(oracle.chunk_attention(cm, q, [(k, v)], 0.4, keep_frames=shuffled), full)
+
+
+def test_dropped_frames_do_not_matter_and_empty_keep_is_segment_attention():
+    S, W, cf, tpf, H, D = 2, 4, 2, 3, 2, 8
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    for c in range(4):
+        cm.append(_rand((cf * tpf, H, D), 100 + c), _rand((cf * tpf, H, D), 110 + c), cf)
+    q, k, v = _rand((cf * tpf, H, D), 120), _rand((cf * tpf, H, D), 121), _rand((cf * tpf, H, D), 122)
+    res = cm.resident()
+    keep = [res[0], res[-1], res[3]]
+    a = oracle.chunk_attention(cm, q, [(k, v)], 0.7, keep_frames=keep)
+    for f in set(res) - set(keep):            # scramble every dropped frame
+        cm.frames[f] = (cm.frames[f][0] * -3 + 1, cm.frames[f][1] + 5)
+    np.testing.assert_array_equal(oracle.chunk_attention(cm, q, [(k, v)], 0.7, keep_frames=keep), a)
+    # nothing retained: plain softmax over the segment alone
+    m = np.ones((cf * tpf, cf * tpf), dtype=bool)
+    ref, _ = dense_masked_softmax(q, k, v, m, 0.7)
+    np.testing.assert_allclose(oracle.chunk_attention(cm, q, [(k, v)], 0.7, keep_frames=[]), ref, atol=1e-12)
+    # one kept frame whose values are one constant row per head, no segment: the output is that row
+    f = res[2]
+    const = _rand((1, H, D), 123)
+    cm.frames[f] = (cm.frames[f][0], np.repeat(const, tpf, axis=0))
+    np.testing.assert_allclose(oracle.chunk_attention(cm, q, [], 0.7, keep_frames=[f]),
+                               np.repeat(const, cf * tpf, axis=0), atol=1e-6)
+
+
+def test_retention_rejects_non_resident_and_repeated_frames():
+    cm = oracle.CacheModel(1, 2, 2, 1, 4, dtype=np.float32)
+    for c in range(3):
+        cm.append(_rand((4, 1, 4), c), _rand((4, 1, 4), 10 + c), 2)
+    q = _rand((2, 1, 4), 5)
+    assert cm.resident() == [0, 4, 5]
+    for bad in ([1], [6], [-1], [0, 0]):
+        with pytest.raises(ValueError):
+            oracle.chunk_attention(cm, q, [], 1.0, keep_frames=bad)
+
+
+# ---------------------------------------------------------------------------------------------
 # MoBA mask
 # ---------------------------------------------------------------------------------------------
 
