@@ -340,3 +340,122 @@ def cross_attention_train(q, k, v, chunk_q_tokens, env_tokens, local_tokens, sca
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
     ivs = [cross_train_row_intervals(int(i), chunk_q_tokens, env_tokens, local_tokens) for i in rows]
     return attend(q[rows], k, v, ivs, scale)
+
+
+# --------------------------------------------------------------------------------------------
+# Quantized QK^T: FP8 e4m3 codes with one fp32 scale per block (the precision-variant of the
+# attention step; "LingBot-World-Infinity" acceleration table: SageAttention 2.2 replaces
+# FlashAttention-2 with a quantized QK^T).  The pages fix no format or block shape; the readings
+# here: OCP e4m3 (largest finite 448), round to nearest even, symmetric absmax scaling per
+# (block of rows, head) -- 32 query rows, 64 keys -- with no smoothing; K blocks are 64
+# consecutive keys of the key sequence in the order the kernel reads it (cache slots in slot
+# order, then the segments); P and V stay bf16/fp32 as in the plain path.
+# --------------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Real value of e4m3 codes (uint8): sign, 4 exponent bits (bias 7), 3 mantissa bits;
+    exponent field 0 is subnormal (m/8 * 2^-6); 0x7f / 0xff are NaN."""
+    c = np.asarray(code).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def e4m3_round(x):
+    """Nearest e4m3 code of float32 values with |x| <= 448 (ties to the even mantissa).
+    The quantum is 2^(e-3) for a value in [2^e, 2^(e+1)), e >= -6, and 2^-9 below 2^-6."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(a)):
+        raise ValueError("e4m3_round takes finite values with |x| <= 448")
+    _, ex = np.frexp(a)                     # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)
+    quantum = np.exp2(e - 3.0)
+    n = np.rint(a / quantum)                # exact division by a power of two; rint ties to even
+    # n lies in [8, 16] for normals (16: carried into the next binade), [0, 8] below 2^-6
+    carry = n >= 16
+    e = np.where(carry, e + 1, e)
+    n = np.where(carry, n / 2, n)
+    normal = n >= 8
+    field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, n - 8, n)
+    code = (field.astype(np.int64) << 3) | mant.astype(np.int64)
+    code = np.where(np.signbit(x), code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def quantize_e4m3_blocks(x, rows):
+    """Per-block FP8 quantization of x [n][H][D] (float32 or bf16 bits): blocks of ``rows``
+    consecutive rows per head (the last one zero-padded).  In fp32: scale = amax / 448,
+    inv = 448 / amax, code = e4m3(clamp(x * inv, -448, 448)); an all-zero block has scale 0
+    and zero codes.  Returns codes [nb][H][rows][D] (uint8) and scales [nb][H] (float32)."""
+    x = widen(x)
+    n, H, D = x.shape
+    nb = -(-n // rows)
+    xp = np.zeros((nb * rows, H, D), np.float32)
+    xp[:n] = x
+    xb = xp.reshape(nb, rows, H, D).transpose(0, 2, 1, 3)            # [nb][H][rows][D]
+    amax = np.max(np.abs(xb), axis=(2, 3)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, np.float32(E4M3_MAX) / amax, np.float32(0)).astype(np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    y = np.clip(xb * inv[:, :, None, None], np.float32(-E4M3_MAX), np.float32(E4M3_MAX)).astype(np.float32)
+    return e4m3_round(y), scale
+
+
+def dequantize_e4m3_blocks(codes, scales, n):
+    """Inverse layout of ``quantize_e4m3_blocks``: fp64 [n][H][D] = value(code) * scale."""
+    nb, H, rows, D = codes.shape
+    v = e4m3_value(codes) * scales.astype(np.float64)[:, :, None, None]
+    return v.transpose(0, 2, 1, 3).reshape(nb * rows, H, D)[:n]
+
+
+def attend_dense_f64(q, k, v, scale):
+    """Unmasked softmax attention of fp64 q [nq][H][D] over k, v [nk][H][D], in numpy fp64
+    (two passes: row max, then exponentials, sum and weighted values)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    out = np.zeros(q.shape, np.float64)
+    if k.shape[0] == 0:
+        return out
+    for hh in range(q.shape[1]):
+        s = (q[:, hh, :] @ k[:, hh, :].T) * scale
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, hh, :] = (p @ v[:, hh, :]) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def kernel_key_sequence(cache, segments):
+    """Keys and values in the order the kernel reads them: the filled cache slots in slot
+    order, then each segment."""
+    ks, vs = [], []
+    if cache is not None:
+        valid = valid_slots(cache.F, cache.S, cache.W)
+        kb, vb = cache.slot_buffers()
+        ks.append(kb[:valid].reshape(-1, cache.H, cache.D))
+        vs.append(vb[:valid].reshape(-1, cache.H, cache.D))
+    for k, v in segments:
+        ks.append(np.asarray(k))
+        vs.append(np.asarray(v))
+    return np.concatenate([widen(x) for x in ks]), np.concatenate([widen(x) for x in vs])
+
+
+def chunk_attention_qk8(cache, q, segments, scale, rows=None):
+    """Chunk attention with the FP8-quantized QK^T: Q quantized in blocks of 32 rows, K in
+    blocks of 64 keys of the kernel's key sequence, softmax and P V exact (fp64) on the
+    dequantized scores.  ``rows`` selects query rows (default: all).  Returns fp64."""
+    k_all, v_all = kernel_key_sequence(cache, segments)
+    q32 = widen(q)
+    qc, qs = quantize_e4m3_blocks(q32, 32)
+    kc, ks = quantize_e4m3_blocks(k_all, 64)
+    qd = dequantize_e4m3_blocks(qc, qs, q32.shape[0])
+    kd = dequantize_e4m3_blocks(kc, ks, k_all.shape[0])
+    if rows is not None:
+        qd = qd[np.asarray(rows)]
+    return attend_dense_f64(qd, kd, v_all, scale)

@@ -652,3 +652,168 @@ def test_generator_c_matches_numpy_and_moments():
     x = synth.normal(1 << 20, dtype="f32", seed=0)
     assert abs(x.mean()) < 5e-3 and abs(x.var() - 65535 / 65536) < 5e-3
     assert x.min() >= -1530 / 256 and x.max() <= 1530 / 256
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 e4m3 quantization of QK^T
+# ---------------------------------------------------------------------------------------------
+
+def _e4m3_by_search(x):
+    """Nearest finite e4m3 value by exhaustive search over the 126 positive magnitudes and
+    zero; a tie goes to the even code."""
+    mags = [(oracle.e4m3_value(np.uint8(c)).item(), c) for c in range(0x7F)]
+    out = []
+    for v in np.asarray(x, np.float32):
+        a = abs(float(v))
+        best = min(abs(a - m) for m, _ in mags)
+        cands = [c for m, c in mags if abs(a - m) == best]
+        c = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        out.append(c | (0x80 if np.signbit(v) else 0))
+    return np.array(out, np.uint8)
+
+
+def test_e4m3_spec_values():
+    """OCP FP8 e4m3 facts: 1.0 = 0x38, largest finite 448 = 0x7e, smallest normal 2^-6 =
+    0x08, smallest subnormal 2^-9 = 0x01, 0x7f is NaN, the sign is the top bit."""
+    v = oracle.e4m3_value(np.array([0x38, 0x7E, 0x08, 0x01, 0x7F, 0xB8, 0x00, 0x80], np.uint8))
+    assert v[0] == 1.0 and v[1] == 448.0 and v[2] == 2.0 ** -6 and v[3] == 2.0 ** -9
+    assert np.isnan(v[4]) and v[5] == -1.0 and v[6] == 0.0 and v[7] == 0.0 and np.signbit(v[7])
+    finite = oracle.e4m3_value(np.arange(256, dtype=np.uint8))
+    assert np.sum(np.isfinite(finite)) == 254
+    pos = np.sort(finite[:0x7F])
+    assert np.all(np.diff(pos) > 0)                    # 127 distinct non-negative values
+
+
+def test_e4m3_round_trips_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_round(oracle.e4m3_value(codes).astype(np.float32)), codes)
+
+
+def test_e4m3_round_matches_nearest_value_search():
+    vals = oracle.e4m3_value(np.arange(0x7F, dtype=np.uint8))
+    pos = np.sort(vals)
+    mids = (pos[:-1] + pos[1:]) / 2                  # every tie, exactly representable in fp32
+    rng = np.random.default_rng(0)
+    x = np.concatenate([mids, -mids, np.nextafter(mids.astype(np.float32), np.float32(1)),
+                        np.nextafter(mids.astype(np.float32), np.float32(-1)),
+                        rng.uniform(-448, 448, 2000), rng.standard_normal(2000) * 0.01,
+                        rng.standard_normal(2000) * 2.0 ** -8, [0.0, -0.0, 448.0, -448.0]]).astype(np.float32)
+    np.testing.assert_array_equal(oracle.e4m3_round(x), _e4m3_by_search(x))
+    with pytest.raises(ValueError):
+        oracle.e4m3_round(np.array([448.5], np.float32))
+
+
+def test_quantize_blocks_scale_and_error_bound():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((150, 3, 64)) * np.array([1.0, 1e-3, 300.0])[None, :, None]).astype(np.float32)
+    x[64:128, 1] = 0.0                                  # an all-zero block
+    codes, scales = oracle.quantize_e4m3_blocks(x, 64)
+    assert codes.shape == (3, 3, 64, 64) and scales.shape == (3, 3)
+    assert scales[1, 1] == 0 and not codes[1, 1].any()
+    xd = oracle.dequantize_e4m3_blocks(codes, scales, 150)
+    for b in range(3):
+        for hh in range(3):
+            blk = x[b * 64:(b + 1) * 64, hh]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            assert scales[b, hh] == np.float32(amax) / np.float32(448)
+            assert np.abs(oracle.e4m3_value(codes[b, hh])).max() == 448.0    # the largest entry hits the top
+            err = np.abs(xd[b * 64:(b + 1) * 64, hh] - blk)
+            # half a quantum: 2^-4 relative in the normal range, 2^-10 * scale below it
+            bound = np.maximum(np.abs(blk) * 2.0 ** -4, 2.0 ** -10 * scales[b, hh]) * (1 + 1e-6)
+            assert np.all(err <= bound)
+
+
+def _lossless(shape, rows, seed):
+    """Values that FP8 block quantization reproduces exactly: random e4m3 grid values with
+    one entry per (block, head) at +-448, times a power of two per block."""
+    rng = np.random.default_rng(seed)
+    n, H, D = shape
+    codes = rng.integers(0, 0x7E, size=shape).astype(np.uint8) | (rng.integers(0, 2, size=shape) << 7).astype(np.uint8)
+    x = oracle.e4m3_value(codes)
+    for b in range(-(-n // rows)):
+        for hh in range(H):
+            x[b * rows, hh, 0] = 448.0
+            x[b * rows:(b + 1) * rows, hh] *= 2.0 ** int(rng.integers(-12, -4))
+    return x.astype(np.float32)
+
+
+def test_qk8_is_exact_on_losslessly_quantizable_inputs():
+    """Per-block power-of-two scales make quantization exact, so the quantized path equals the
+    plain attention; a wrong block partition (of Q rows, or of the kernel's key sequence)
+    would mix two blocks' scales and lose bits."""
+    S, W, cf, tpf, H, D = 2, 3, 2, 24, 2, 64
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    for c in range(5):                                   # ring wrapped: slot order != time order
+        cm.append(_rand((cf * tpf, H, D), 200 + c), _rand((cf * tpf, H, D), 210 + c), cf)
+    k_seq, _ = oracle.kernel_key_sequence(cm, [])
+    nk = k_seq.shape[0]
+    kl = _lossless((nk + 40, H, D), 64, 3)               # the kernel-order keys, then a segment
+    valid = oracle.valid_slots(cm.F, S, W)
+    for s, f in enumerate(cm.slot_map()[:valid]):
+        cm.frames[f] = (kl[s * tpf:(s + 1) * tpf], cm.frames[f][1])
+    seg_k, seg_v = kl[nk:], _rand((40, H, D), 220)
+    q = _lossless((70, H, D), 32, 4)
+    a = oracle.chunk_attention_qk8(cm, q, [(seg_k, seg_v)], 0.05)
+    b = oracle.chunk_attention(cm, q, [(seg_k, seg_v)], 0.05)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # one extra key ahead of the segment shifts its rows against the 64-key blocks: lossy
+    extra = [(np.full((1, H, D), 0.5, np.float32), seg_v[:1]), (seg_k, seg_v)]
+    c = oracle.chunk_attention_qk8(cm, q, extra, 0.05)
+    assert np.abs(c - oracle.chunk_attention(cm, q, extra, 0.05)).max() > 1e-9
+    cm2_frames = dict(cm.frames)
+    f0 = cm.slot_map()[0]
+    kk = cm.frames[f0][0].copy()
+    kk[0, :, 0] *= 3.0                                   # one key 3x larger: its block's scale moves
+    cm.frames[f0] = (kk, cm.frames[f0][1])
+    d = oracle.chunk_attention_qk8(cm, q, [(seg_k, seg_v)], 0.05)
+    e = oracle.chunk_attention(cm, q, [(seg_k, seg_v)], 0.05)
+    assert np.abs(d - e).max() > 1e-9
+    cm.frames = cm2_frames
+
+
+def test_kernel_key_sequence_is_slot_order():
+    S, W, cf, tpf, H, D = 2, 3, 2, 5, 1, 8
+    cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    for c in range(5):
+        cm.append(_rand((cf * tpf, H, D), 300 + c), _rand((cf * tpf, H, D), 310 + c), cf)
+    k, v = oracle.kernel_key_sequence(cm, [(np.ones((3, H, D), np.float32), np.zeros((3, H, D), np.float32))])
+    slots = cm.slot_map()
+    valid = oracle.valid_slots(cm.F, S, W)
+    assert k.shape[0] == valid * tpf + 3
+    for s in range(valid):
+        np.testing.assert_array_equal(k[s * tpf:(s + 1) * tpf], cm.frames[slots[s]][0])
+        np.testing.assert_array_equal(v[s * tpf:(s + 1) * tpf], cm.frames[slots[s]][1])
+    assert sorted(slots[:valid]) != list(slots[:valid])   # the ring has wrapped: not time order
+    np.testing.assert_array_equal(k[-3:], 1.0)
+
+
+def test_dense_f64_attention_matches_c_core():
+    q, k, v = _rand((9, 3, 32), 400), _rand((50, 3, 32), 401), _rand((50, 3, 32), 402)
+    a = oracle.attend_dense_f64(q, k, v, 0.3)
+    b = oracle.attend(q, k, v, [[(0, 50)]] * 9, 0.3)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_qk8_error_against_exact_attention_is_small():
+    """The quantization error itself, at N(0,1) inputs with a 832x464-like key count per
+    head (cache + current chunk, 2 heads): the looser bound of the quantized path."""
+    S, W, cf, tpf, H, D = 6, 8, 4, 48, 2, 128
+    cm = oracle.CacheModel(S, W, tpf, H, D)
+    for c in range(5):
+        cm.append(synth.normal(cf * tpf * H * D, seed=9, chunk=c, kind=synth.KFIN).reshape(cf * tpf, H, D),
+                  synth.normal(cf * tpf * H * D, seed=9, chunk=c, kind=synth.VFIN).reshape(cf * tpf, H, D), cf)
+    q, k, v = (synth.normal(cf * tpf * H * D, seed=10, kind=t).reshape(cf * tpf, H, D)
+               for t in (synth.Q, synth.K, synth.V))
+    a = oracle.chunk_attention_qk8(cm, q, [(k, v)], 1 / np.sqrt(D))
+    b = oracle.chunk_attention(cm, q, [(k, v)], 1 / np.sqrt(D))
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel < QK8_REL_L2_VS_EXACT, rel
+    assert np.abs(a - b).max() < QK8_MAX_ABS_VS_EXACT
+
+
+# bounds of the quantized path against exact attention (N(0,1) inputs, D = 128): e4m3 keeps
+# 3 mantissa bits, so each score carries an error of a few percent of its magnitude
+QK8_REL_L2_VS_EXACT = 0.1
+QK8_MAX_ABS_VS_EXACT = 0.05
