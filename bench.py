@@ -270,6 +270,24 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps):
     del c, q, k, v, o
     torch.cuda.empty_cache()
 
+    # FP8-quantized QK^T at 832x464: warm cache + the current chunk; one call =
+    # quantization of Q and of the key sequence, then the attention kernel
+    c8 = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S, window_frames=W,
+                   chunk_frames=CF)
+    nq8 = CF * TPF
+    for i in range(4):
+        c8.append_evict(0, fill((nq8, H, D), chunk=i, step=4, kind=synth.KFIN),
+                        fill((nq8, H, D), chunk=i, step=4, kind=synth.VFIN), CF)
+    q8, k8, v8 = (fill((nq8, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
+    o8 = torch.empty_like(q8)
+    f8 = 4.0 * D * H * nq8 * (S + W + CF) * TPF
+    avg, mn = timed(lambda: wmk.chunk_attention_qk8(c8, 0, q8, [(k8, v8)], out=o8))
+    res["832x464_qk8"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(f8 / avg / 1e9, 1),
+                          "frac_peak_bf16": round(f8 / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                          "note": "QK^T in fp8 e4m3 (per-block scales, quantization passes included), P V in bf16"}
+    del c8, q8, k8, v8, o8
+    torch.cuda.empty_cache()
+
     # rolling session at 832x464: 30 layers x 4 denoising steps per chunk over a
     # full 18-slot cache, then the finalized chunk appended to every layer
     layers, steps = 30, 4

@@ -170,6 +170,36 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
                                int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes for wmk_chunk_attention_qk8 with q_tokens queries and up to
+ * kv_tokens keys (cache part plus segments): the FP8 codes and scales of Q and
+ * K, plus the optional split-tail scratch of wmk_attention_workspace_bytes.
+ * 0 if hd is invalid, not bf16 or head_dim is not 128. */
+size_t wmk_attention_qk8_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens, int64_t kv_tokens);
+
+/* Chunk attention with a quantized QK^T: as wmk_chunk_attention, but the
+ * scores S = Q K^T come from FP8 (OCP e4m3) operands with one fp32 scale per
+ * block -- the precision variant of the attention step ("LingBot-World-
+ * Infinity" acceleration table: an INT8-QK^T SageAttention kernel replaces
+ * FlashAttention-2; this build quantizes to FP8 for the CDNA4 matrix cores).
+ * Per head, Q is cut into blocks of 32 rows and the keys -- cache slots in
+ * slot order, then the segments -- into tiles of 64; per block, in fp32:
+ * scale = max|x| / 448, code = e4m3(clamp(x * 448 / max|x|, +-448)), nearest
+ * even (all zero: scale 0, codes 0).  Softmax, P (bf16) and P V (bf16, fp32
+ * accumulate) are as in the plain path.
+ * The workspace is required and holds, from its start (256-byte aligned), the
+ * K codes ([tile][head][64][128] bytes, the 16-byte chunks of row r permuted
+ * by XOR with (r / 2) % 8), the K scales ([tile][head] fp32), the Q codes
+ * ([block][head][32][128] bytes, row-major) and the Q scales, each region
+ * 256-byte aligned; any rest serves the split tail.  Contents are overwritten
+ * on every call.  bf16 and head_dim 128 only.
+ * Errors: as wmk_chunk_attention, plus dtype not bf16 -> WMK_ERR_DTYPE,
+ * head_dim not 128 -> WMK_ERR_SHAPE, workspace NULL or smaller than
+ * wmk_attention_qk8_workspace_bytes minus the split scratch ->
+ * WMK_ERR_CAPACITY, workspace not 256-byte aligned -> WMK_ERR_ALIGN. */
+wmk_status wmk_chunk_attention_qk8(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
+                                   int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Chunk attention with variable retention: as wmk_chunk_attention, but of
  * the resident frames of `layer` only the n_keep listed in keep_frames (a
  * host array of global frame indices, any order, as reported by

@@ -61,6 +61,11 @@ _SIGNATURES = {
     "wmk_chunk_attention": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
                                            ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P, ctypes.c_float, _P,
                                            ctypes.c_size_t, _P]),
+    "wmk_attention_qk8_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_head_desc), ctypes.c_int32,
+                                                            ctypes.c_int64]),
+    "wmk_chunk_attention_qk8": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
+                                               ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P, ctypes.c_float,
+                                               _P, ctypes.c_size_t, _P]),
     "wmk_chunk_attention_retained": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                                     ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
                                                     ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P,
@@ -236,6 +241,39 @@ def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_work
         _check(load().wmk_chunk_attention_retained(cache.handle if cache is not None else None, layer, arr,
                                                    len(keep), ctypes.byref(hd), _ptr(q), nq, segs, len(segments),
                                                    _ptr(out), scale, ws, wsb, _stream_ptr(stream)))
+    return out
+
+
+def qk8_workspace_bytes(num_heads, q_tokens, kv_tokens, head_dim=128):
+    """Bytes of workspace chunk_attention_qk8 needs (quantized operands + split scratch)."""
+    hd = wmk_head_desc(num_heads, head_dim, WMK_BF16)
+    return load().wmk_attention_qk8_workspace_bytes(ctypes.byref(hd), q_tokens, kv_tokens)
+
+
+def chunk_attention_qk8(cache, layer, q, segments=(), out=None, scale=None, stream=None, ws=None):
+    """chunk_attention with the FP8-quantized QK^T.  ``ws``: a uint8 device tensor to use as
+    the workspace (its head then holds the quantized operands, see include/wmk.h); by
+    default a cached one sized for every resident frame plus the segments."""
+    torch = _torch()
+    nq, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    segs = (wmk_kv_segment * max(1, len(segments)))()
+    kv = 0
+    for i, (k, v) in enumerate(segments):
+        segs[i] = wmk_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[0])
+        kv += k.shape[0]
+    if cache is not None:
+        kv += (cache.desc.sink_frames + cache.desc.window_frames) * cache.desc.tokens_per_frame
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if ws is None:
+        wsb = load().wmk_attention_qk8_workspace_bytes(ctypes.byref(hd), nq, kv)
+        ws = workspace(q.device, wsb) if wsb else None
+    wsp, wsb = (_ptr(ws), ws.numel()) if ws is not None else (ctypes.c_void_p(0), 0)
+    _check(load().wmk_chunk_attention_qk8(cache.handle if cache is not None else None, layer, ctypes.byref(hd),
+                                          _ptr(q), nq, segs, len(segments), _ptr(out), scale, wsp, wsb,
+                                          _stream_ptr(stream)))
     return out
 
 

@@ -34,6 +34,12 @@
 // the workgroup allows are never visited: the workgroup walks only the union of
 // its rows' ranges, in tile units.
 //
+// FP8 variant (Q8): Q and K arrive pre-quantized to e4m3 with one fp32 scale per
+// block (32 query rows of a wave; one 64-key tile), the K tile already in the
+// LDS layout below; S^T = K Q^T runs as v_mfma_scale_f32_32x32x64_f8f6f4 (two
+// k-steps of 64 dims instead of eight of 16) and the block scales fold into the
+// per-tile exponent multiplier.  Softmax, P and P V are as in the bf16 path.
+//
 // Sources: chunk attention over [anchors | recent | current] ("Westlake AGI
 // Lab's 'World in World' Steers Frozen Video Models", second paragraph); the
 // MoBA mask ("Infinite Worlds with Versatile Interactions", causal pretraining
@@ -58,6 +64,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -467,6 +474,51 @@ __device__ __forceinline__ bf16x8 v_frag(const Buf<D>& vbuf, const LdsAddr<D>& l
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---- FP8 QK^T (head_dim 128): a K tile of 64 keys x 128 one-byte codes (8 KB)
+// in one LDS object; the 16-byte chunks of row r XOR-permuted by (r / 2) % 8, so
+// the 16 lanes of a read phase (rows r..r+15, one logical chunk) hit distinct
+// banks.  A-operand fragment of key block kb, k-step ks: lane (l32, h) holds row
+// 32 kb + l32, dims 64 ks + 32 h .. + 31 (two chunks); the B operand (Q^T) uses
+// the same dims per lane, which is all the contraction needs.
+constexpr int kD8 = 128;
+constexpr int kTile8 = BK * kD8;          // bytes of one K8 tile
+constexpr int kDS8 = kD8 / 64;            // k-steps of 64 dims
+
+__device__ __forceinline__ uint32_t k8_off(int l32, int h, int ks, int half) {
+    const int chunk = 4 * ks + 2 * h + half;
+    return (uint32_t)(l32 * kD8 + ((chunk ^ ((l32 >> 1) & 7)) * 16));
+}
+
+// rows 32..63 sit 4 KB further with the same permutation ((32 + r) / 2 % 8 = r / 2 % 8)
+template <int KB>
+__device__ __forceinline__ i32x8 k8_frag(const char LDS_AS* buf, const uint32_t* off, int ks) {
+    const u32x4 a = *(const u32x4 LDS_AS*)(buf + KB * 32 * kD8 + off[2 * ks]);
+    const u32x4 b = *(const u32x4 LDS_AS*)(buf + KB * 32 * kD8 + off[2 * ks + 1]);
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// e4m3 x e4m3 -> fp32, unit block scales (E8M0 exponent 127 = 2^0)
+__device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// S^T = K Q^T for one FP8 tile (two blocks of 32 keys) from an LDS buffer.
+__device__ __forceinline__ void qk_tile8(const char LDS_AS* kbuf, const i32x8* qf8, const uint32_t* off, f32x16* s) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kDS8; ++ks) {
+        s[0] = mfma8(k8_frag<0>(kbuf, off, ks), qf8[ks], s[0]);
+        s[1] = mfma8(k8_frag<1>(kbuf, off, ks), qf8[ks], s[1]);
+    }
+}
+
+// One fp32 read through the vector memory path (counted with the direct loads,
+// so the waits for LDS reads that follow need not drain it); 0 when !ok.
+__device__ __forceinline__ float load_f32_vmem(const float* ptr, bool ok) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ptr, ok ? 4u : 0u), 0, 0, 0));
+}
+
 // Workspace of the split tail: per split unit a counter, then per piece the
 // unnormalized O (BQ x D fp32) and per-row (max reference, sum).
 template <int D>
@@ -479,9 +531,11 @@ struct SplitWs {
     }
 };
 
-template <int D, int NS>
+template <int D, int NS, bool Q8>
 __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     using C = Cfg<D>;
+    static_assert(!Q8 || D == kD8, "FP8 QK^T is built for head_dim 128");
+    static_assert(!Q8 || C::PARTB == kTile8, "a K8 tile fills the first LDS object of a K buffer");
     const AttnCallN<NS>& c = prm.c;
     const AttnPlan& p = prm.p;
     // Separate LDS objects, each named statically in the unrolled loop below
@@ -489,9 +543,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     // by direct loads from the ones being read -- and the direct loads of one
     // tile from each other -- and adds no waits between them.
     __shared__ __attribute__((aligned(1024))) char k0p0[C::PARTB];
-    __shared__ __attribute__((aligned(1024))) char k0p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char k0p1[C::LPT > 1 && !Q8 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char k1p0[C::PARTB];
-    __shared__ __attribute__((aligned(1024))) char k1p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char k1p1[C::LPT > 1 && !Q8 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char v0p0[C::PARTB];
     __shared__ __attribute__((aligned(1024))) char v0p1[C::LPT > 1 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char v1p0[C::PARTB];
@@ -559,8 +613,23 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     const int64_t stride = (int64_t)c.heads * D;
 
     // Q^T fragments (B operand): lane owns query l32, dims ds*16 + h*8 .. +7
-    bf16x8 qf[C::DS];
-    {
+    // (FP8: dims 64 ks + 32 h .. + 31 of the wave's quantized 32-row block)
+    bf16x8 qf[Q8 ? 1 : C::DS];
+    [[maybe_unused]] i32x8 qf8[kDS8];
+    float cs0 = c.scale * kLog2e;
+    if constexpr (Q8) {
+        if (wave_has_rows) {
+            const size_t qb = (size_t)(qt * NW + wave) * c.heads + head;
+            const uint8_t* qp = p.q8 + qb * 32 * D + l32 * D + h * 32;
+#pragma unroll
+            for (int ks = 0; ks < kDS8; ++ks) {
+                const u32x4 a = *(const u32x4*)(qp + ks * 64), b2 = *(const u32x4*)(qp + ks * 64 + 16);
+                qf8[ks] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b2[0], (int)b2[1], (int)b2[2], (int)b2[3]};
+            }
+            const float sq = p.q8_scale[qb];
+            cs0 *= sq > 0.0f ? sq : 1.0f;  // an all-zero block has zero codes: any positive factor
+        }
+    } else {
         const __bf16* qp = (const __bf16*)c.q + (int64_t)row * stride + (int64_t)head * D + h * 8;
 #pragma unroll
         for (int ds = 0; ds < C::DS; ++ds) {
@@ -573,7 +642,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] = f32x16{};
     float m_ref = -INFINITY, l_run = 0.0f;
-    const float cs = c.scale * kLog2e;
+    // exponent multipliers (scale * log2 e, times the block scales with FP8) of
+    // the tile being finished (cs_a) and of the next one (cs_b)
+    float cs_a = cs0, cs_b = cs0;
+    auto k8_scale = [&](int32_t tile) __attribute__((always_inline)) -> float {
+        const float sk = p.k8_scale[(size_t)tile * c.heads + head];
+        return sk > 0.0f ? sk : 1.0f;  // an all-zero tile has zero codes: any positive factor
+    };
     const LoadMap<D> lm = load_map<D>(wave, (uint32_t)(c.heads * D * 2));
     const LdsAddr<D> la = lds_addr<D>(lane);
 
@@ -618,7 +693,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-        const float mt = pair_max(mx) * cs;
+        const float mt = pair_max(mx) * cs_a;
         const bool grow = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
         const float m_new = grow ? fmaxf(m_ref, mt) : m_ref;
         const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -631,7 +706,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         constexpr int kb = decltype(kb_c)::value, t = decltype(t_c)::value;
         f32x8 e;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs, -m_use));
+        for (int r = 0; r < 8; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + r], cs_a, -m_use));
         const bf16x8 p8 = __builtin_convertvector(e, bf16x8);
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
@@ -649,14 +724,42 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     Cursor vcu = cursor_at(c, tr, it0, row_bytes, head_off);
     const int32_t tile0 = vcu.tile;
     Cursor kcu = vcu;
+    // FP8: a K tile is one contiguous 8 KB block, copied as it stands (wave w
+    // moves bytes [1 KB w, 1 KB (w + 1))); per-lane fragment offsets
+    [[maybe_unused]] const uint32_t k8_lane = (uint32_t)(wave * 1024 + lane * 16);
+    [[maybe_unused]] uint32_t k8o[2 * kDS8];
+    if constexpr (Q8) {
+#pragma unroll
+        for (int ks = 0; ks < kDS8; ++ks) {
+            k8o[2 * ks] = k8_off(l32, h, ks, 0);
+            k8o[2 * ks + 1] = k8_off(l32, h, ks, 1);
+        }
+    }
+    auto k8_src = [&](int32_t tile) __attribute__((always_inline)) {
+        return p.k8 + ((size_t)tile * c.heads + head) * kTile8;
+    };
     if (it0 < it1) {
-        issue_tile<D>(c, head, vcu, lm, wave, kb0, vb0, true, true);
+        if constexpr (Q8) {
+            dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane, kb0.part[0] + wave * 1024);
+            issue_tile<D>(c, head, vcu, lm, wave, kb0, vb0, false, true);
+            cs_a = cs0 * k8_scale(vcu.tile);
+        } else {
+            issue_tile<D>(c, head, vcu, lm, wave, kb0, vb0, true, true);
+        }
         advance(vcu, c, tr, it0 + 1, row_bytes, head_off);
-        if (it0 + 1 < it1) issue_tile<D>(c, head, vcu, lm, wave, kb1, vb1, true, false);
+        if (it0 + 1 < it1) {
+            if constexpr (Q8) {
+                dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane, kb1.part[0] + wave * 1024);
+                cs_b = cs0 * k8_scale(vcu.tile);
+            } else {
+                issue_tile<D>(c, head, vcu, lm, wave, kb1, vb1, true, false);
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (wave_has_rows) {
-            qk_tile<D>(kb0, qf, la, s);
+            if constexpr (Q8) qk_tile8(kb0.part[0], qf8, k8o, s);
+            else qk_tile<D>(kb0, qf, la, s);
             mask_tile(tile0);
             new_ref();  // O and l are still zero
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -687,13 +790,22 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         // per span; its pieces then fetch nothing (zero-size resource) into a
         // dummy block, as do those of a tile past the range.
         const bool k_ok = it + 2 < it1, v_ok = it + 1 < it1;
-        const bool k_fast = k_ok && kcu.run > 0, v_fast = v_ok && vcu.run > 0;
-        if (k_ok && !k_fast) issue_tile<D>(c, head, kcu, lm, wave, kcur, vnext, true, false);
+        const bool k_fast = k_ok && (Q8 || kcu.run > 0), v_fast = v_ok && vcu.run > 0;
+        if constexpr (!Q8) {
+            if (k_ok && !k_fast) issue_tile<D>(c, head, kcu, lm, wave, kcur, vnext, true, false);
+        }
         if (v_ok && !v_fast) issue_tile<D>(c, head, vcu, lm, wave, kcur, vnext, false, true);
-        const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kcu.k, k_fast ? tile_bytes : 0u);
+        const __amdgpu_buffer_rsrc_t krs =
+            Q8 ? buffer_rsrc(k8_src(k_ok ? kcu.tile : 0), k_ok ? (uint32_t)kTile8 : 0u)
+               : buffer_rsrc(kcu.k, k_fast ? tile_bytes : 0u);
         const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vcu.v, v_fast ? tile_bytes : 0u);
+        // FP8: the block scale of K(it+2), used from the next step on
+        [[maybe_unused]] float sk_next = 1.0f;
+        if constexpr (Q8 && !LAST)
+            sk_next = load_f32_vmem(p.k8_scale + (size_t)(k_ok ? kcu.tile : 0) * c.heads + head, k_ok);
         auto k_piece = [&](int i) __attribute__((always_inline)) {
-            dma16(krs, lm.kg[i], (k_fast ? kcur.part[i] : (char LDS_AS*)dummy) + wave * 1024);
+            if constexpr (Q8) dma16(krs, k8_lane, (k_ok ? kcur.part[0] : (char LDS_AS*)dummy) + wave * 1024);
+            else dma16(krs, lm.kg[i], (k_fast ? kcur.part[i] : (char LDS_AS*)dummy) + wave * 1024);
         };
         auto v_piece = [&](int i) __attribute__((always_inline)) {
             dma16(vrs, lm.vg[i], (v_fast ? vnext.part[i] : (char LDS_AS*)dummy) + wave * 1024);
@@ -704,7 +816,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         if (!wave_has_rows && !LAST) {
 #pragma unroll
             for (int i = 0; i < C::LPT; ++i) {
-                k_piece(i);
+                if (!Q8 || i == 0) k_piece(i);
                 v_piece(i);
             }
         }
@@ -719,7 +831,33 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             constexpr int EPS = 16 / C::DS;  // weights of s[1] per k-step
             f32x16 sn0 = f32x16{}, sn1 = f32x16{};
             f32x8 e0, e1;
-            if constexpr (!LAST) {
+            if constexpr (!LAST && Q8) {
+                // FP8: all four fragments of K(it+1) up front, two k-steps of 64 dims
+                const char LDS_AS* kn = knext.part[0];
+                i32x8 ka8[kDS8][2];
+#pragma unroll
+                for (int ks = 0; ks < kDS8; ++ks) {
+                    ka8[ks][0] = k8_frag<0>(kn, k8o, ks);
+                    ka8[ks][1] = k8_frag<1>(kn, k8o, ks);
+                }
+                constexpr int EPS8 = 16 / kDS8;
+#pragma unroll
+                for (int ks = 0; ks < kDS8; ++ks) {
+                    sn0 = mfma8(ka8[ks][0], qf8[ks], sn0);
+                    if (ks == 0) k_piece(0);
+#pragma unroll
+                    for (int i = 0; i < C::LPT; ++i)
+                        if (i * kDS8 / C::LPT == ks) v_piece(i);
+#pragma unroll
+                    for (int x = 0; x < EPS8; ++x) {
+                        const int idx = ks * EPS8 + x;
+                        const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs_a, -m_use));
+                        if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
+                    }
+                    sn1 = mfma8(ka8[ks][1], qf8[ks], sn1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else if constexpr (!LAST) {
                 const char LDS_AS* kn0 = knext.template block_row<0>(0);
                 const char LDS_AS* kn1 = knext.template block_row<1>(0);
                 bf16x8 ka[KPF + 1][2];
@@ -740,7 +878,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 #pragma unroll
                     for (int x = 0; x < EPS; ++x) {
                         const int idx = ds * EPS + x;
-                        const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs, -m_use));
+                        const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs_a, -m_use));
                         if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
                     }
                     sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][1], qf[ds], sn1, 0, 0, 0);
@@ -749,7 +887,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             } else {
 #pragma unroll
                 for (int idx = 0; idx < 16; ++idx) {
-                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs, -m_use));
+                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][idx], cs_a, -m_use));
                     if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
                 }
             }
@@ -809,7 +947,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 #pragma unroll
                             for (int r = i * (32 / RMX); r < (i + 1) * (32 / RMX); ++r) mx = fmaxf(mx, s[r / 16][r % 16]);
                         } else if constexpr (i == SREF) {
-                            const float mt = pair_max(mx) * cs;
+                            const float mt = pair_max(mx) * cs_b;
                             grow = __builtin_amdgcn_ballot_w64(mt > m_ref + kTau) != 0;
                             const float m_new = grow ? fmaxf(m_ref, mt) : m_ref;
                             alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -819,7 +957,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 #pragma unroll
                             for (int r = 0; r < 16; ++r)
                                 if (WFIRST + r * WSLOTS / 16 == i) {
-                                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], cs, -m_next));
+                                    const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][r], cs_b, -m_next));
                                     if (r < 8) w0[r] = v; else w1[r - 8] = v;
                                 }
                         } else if constexpr (i == NPV - 1) {
@@ -854,6 +992,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if constexpr (Q8 && !LAST) {
+            cs_a = cs_b;
+            cs_b = cs0 * (sk_next > 0.0f ? sk_next : 1.0f);
+        }
     };
     int32_t it = it0;
     for (; it + 2 < it1; it += 2) {
@@ -971,9 +1113,9 @@ int attn_bf16_blocks_per_cu(int head_dim) {
     int n = 0;
     hipError_t e;
     if (head_dim == 64)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kFewSeg>, NT, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kFewSeg, false>, NT, 0);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, kFewSeg>, NT, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, kFewSeg, false>, NT, 0);
     return (e == hipSuccess && n > 0) ? n : 1;
 }
 
@@ -996,10 +1138,12 @@ hipError_t launch_spans(const AttnCall& c, const AttnPlan& plan, int32_t blocks,
     }
     prm.c.kv.n = c.kv.n;
     prm.p = plan;
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, NS>), dim3(blocks), dim3(NT), 0, s, prm);
+    if (plan.k8 != nullptr)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, true>), dim3(blocks), dim3(NT), 0, s, prm);
+    else if (c.head_dim == 64)
+        hipLaunchKernelGGL((attn_bf16_kernel<64, NS, false>), dim3(blocks), dim3(NT), 0, s, prm);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<128, NS>), dim3(blocks), dim3(NT), 0, s, prm);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, false>), dim3(blocks), dim3(NT), 0, s, prm);
     return hipGetLastError();
 }
 
@@ -1007,6 +1151,9 @@ hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t
     const int32_t blocks = plan.n_units - plan.split_units + plan.split_units * plan.splits;
     if (blocks <= 0) return hipSuccess;
     if (c.kv.n < 0 || c.kv.n > kMaxSeg || (c.head_dim != 64 && c.head_dim != 128)) return hipErrorInvalidValue;
+    if (plan.k8 != nullptr && (c.head_dim != 128 || plan.q8 == nullptr || plan.k8_scale == nullptr ||
+                               plan.q8_scale == nullptr))
+        return hipErrorInvalidValue;
     if (plan.split_units > 0) {
         hipLaunchKernelGGL(zero_ints, dim3((plan.split_units + 255) / 256), dim3(256), 0, s, (int*)plan.ws,
                            plan.split_units);

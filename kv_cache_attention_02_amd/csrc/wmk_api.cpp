@@ -234,8 +234,16 @@ void plan_moba_groups(wmk::AttnPlan& p, const wmk::MaskShape& m, int32_t q_token
     p.n_groups = (int32_t)runs.size();
 }
 
+// FP8 QK^T buffers carved from the caller's workspace (see qk8_layout).
+struct Qk8Bufs {
+    uint8_t* k8;
+    float* k8_scale;
+    uint8_t* q8;
+    float* q8_scale;
+};
+
 wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, size_t ws_bytes,
-                         hipStream_t stream) {
+                         hipStream_t stream, const Qk8Bufs* qk8 = nullptr) {
     if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
     hipError_t e;
     if (dtype == WMK_F32) {
@@ -265,15 +273,33 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
             p.xcd_remap = 1;
             plan_split(p, call.head_dim, tiles, ws, ws_bytes);
         }
+        if (qk8 != nullptr) {
+            p.k8 = qk8->k8;
+            p.k8_scale = qk8->k8_scale;
+            p.q8 = qk8->q8;
+            p.q8_scale = qk8->q8_scale;
+        }
         if (dry_run_path() != nullptr) {
             dry_log("attn dtype=bf16 q=%d heads=%d d=%d kv=%d mask=%d bq=%d units=%d qtiles=%d groups=%d "
-                    "split_units=%d splits=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total,
-                    call.mask.mode, bq, p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits);
+                    "split_units=%d splits=%d qk8=%d\n", call.q_tokens, call.heads, call.head_dim, call.kv_total,
+                    call.mask.mode, bq, p.n_units, p.n_qtiles, p.n_groups, p.split_units, p.splits,
+                    qk8 != nullptr ? 1 : 0);
             for (int g = 0; g < p.n_groups; ++g) dry_log("group %d %d\n", p.grp_start[g], p.grp_count[g]);
             for (int x = 0; x < call.kv.n; ++x)
                 dry_log("span %d %d %llx %llx\n", x, call.kv.end[x], (unsigned long long)(uintptr_t)call.kv.k[x],
                         (unsigned long long)(uintptr_t)call.kv.v[x]);
             return ok();
+        }
+        if (qk8 != nullptr) {
+            // quantize Q (blocks of 32 rows) and the key sequence (tiles of 64 keys) first
+            const void* qsrc[1] = {call.q};
+            const int32_t qend[1] = {call.q_tokens};
+            e = wmk::launch_quant_e4m3(qsrc, qend, 1, call.q_tokens, call.heads, call.head_dim, 32, qk8->q8,
+                                       qk8->q8_scale, stream);
+            if (e == hipSuccess && call.kv_total > 0)
+                e = wmk::launch_quant_e4m3(call.kv.k, call.kv.end, call.kv.n, call.kv_total, call.heads,
+                                           call.head_dim, 64, qk8->k8, qk8->k8_scale, stream);
+            if (e != hipSuccess) return fail(WMK_ERR_HIP, "quantization launch failed: %s", hipGetErrorString(e));
         }
         e = wmk::launch_attn_bf16(call, p, stream);
     }
@@ -283,6 +309,31 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
 
 const int64_t kNoFrame = -1;
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the FP8 QK^T path, in order: K codes (one 8 KB block per 64-key
+// tile and head), their scales, Q codes (one 4 KB block per 32 rows and head),
+// their scales -- each 256-byte aligned -- then the split-tail scratch.
+size_t qk8_bytes(int32_t heads, int32_t q_tokens, int64_t kv_tokens, Qk8Bufs* b, char* base) {
+    const int64_t kt = (kv_tokens + 63) / 64, qb = ((int64_t)q_tokens + 31) / 32;
+    size_t off = 0;
+    const size_t k8 = off;
+    off += align256((size_t)kt * heads * 64 * 128);
+    const size_t ks = off;
+    off += align256((size_t)kt * heads * 4);
+    const size_t q8 = off;
+    off += align256((size_t)qb * heads * 32 * 128);
+    const size_t qs = off;
+    off += align256((size_t)qb * heads * 4);
+    if (b != nullptr) {
+        b->k8 = (uint8_t*)(base + k8);
+        b->k8_scale = (float*)(base + ks);
+        b->q8 = (uint8_t*)(base + q8);
+        b->q8_scale = (float*)(base + qs);
+    }
+    return off;
+}
+
 // Chunk attention over the resident frames of `layer` (keep == NULL: all of
 // them; else the n_keep listed frames) plus the caller's segments.  The cache
 // part becomes one span per run of adjacent selected slots, in slot order:
@@ -290,9 +341,11 @@ const int64_t kNoFrame = -1;
 wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t* keep, int32_t n_keep,
                                 const wmk_head_desc* hd, const void* q, int32_t q_tokens, const wmk_kv_segment* seg,
                                 int32_t n_seg, void* out, float scale, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool qk8 = false) {
     wmk_status s = check_head(hd);
     if (s != WMK_OK) return s;
+    if (qk8 && hd->dtype != WMK_BF16) return fail(WMK_ERR_DTYPE, "FP8 QK^T takes bf16 inputs");
+    if (qk8 && hd->head_dim != 128) return fail(WMK_ERR_SHAPE, "FP8 QK^T is built for head_dim 128");
     if (q == nullptr || out == nullptr) return fail(WMK_ERR_NULL, "q and out must not be NULL");
     if (n_seg < 0 || n_seg > wmk::kMaxCallerSeg)
         return fail(WMK_ERR_SHAPE, "n_seg %d outside [0, %d]", n_seg, wmk::kMaxCallerSeg);
@@ -366,7 +419,13 @@ wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t
     call.kv_total = (int32_t)total;
     call.scale = scale;
     call.mask.mode = wmk::kMaskNone;
-    return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
+    if (!qk8) return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
+    Qk8Bufs bufs;
+    const size_t need = qk8_bytes(hd->num_heads, q_tokens, total, &bufs, (char*)workspace);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(WMK_ERR_CAPACITY, "FP8 QK^T needs %zu bytes of workspace, got %zu", need, workspace_bytes);
+    if (((uintptr_t)workspace & 255) != 0) return fail(WMK_ERR_ALIGN, "workspace must be 256-byte aligned");
+    return run_attention(call, hd->dtype, (char*)workspace + need, workspace_bytes - need, stream, &bufs);
 }
 
 }  // namespace
@@ -500,6 +559,21 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_attention_impl(c, layer, nullptr, 0, hd, q, q_tokens, seg, n_seg, out, scale, workspace,
                                 workspace_bytes, stream);
+}
+
+size_t wmk_attention_qk8_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens, int64_t kv_tokens) {
+    if (check_head(hd) != WMK_OK || hd->dtype != WMK_BF16 || hd->head_dim != 128 || q_tokens <= 0 || kv_tokens < 0 ||
+        kv_tokens > INT32_MAX)
+        return 0;
+    return qk8_bytes(hd->num_heads, q_tokens, kv_tokens, nullptr, nullptr) +
+           wmk_attention_workspace_bytes(hd, q_tokens);
+}
+
+wmk_status wmk_chunk_attention_qk8(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
+                                   int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return chunk_attention_impl(c, layer, nullptr, 0, hd, q, q_tokens, seg, n_seg, out, scale, workspace,
+                                workspace_bytes, stream, true);
 }
 
 wmk_status wmk_chunk_attention_retained(const wmk_cache* c, int32_t layer, const int64_t* keep_frames,

@@ -75,6 +75,14 @@ struct AttnPlan {
     int32_t split_units;
     int32_t splits;
     void* ws;               // workspace for the split tail (may be NULL when split_units == 0)
+    // FP8 QK^T (all NULL for the bf16 product): e4m3 codes of Q in blocks of 32
+    // rows and of K in blocks of 64 keys (one tile, stored in the kernel's LDS
+    // layout), each block [rows][head_dim] per (block, head), and the fp32 scale
+    // of each block at [block * heads + head]
+    const uint8_t* q8;
+    const float* q8_scale;
+    const uint8_t* k8;
+    const float* k8_scale;
 };
 
 // bf16 MFMA attention.  Returns the launch status.
@@ -88,6 +96,13 @@ int attn_bf16_blocks_per_cu(int head_dim);
 
 // Workspace bytes the bf16 kernel's split tail needs for `pieces` pieces.
 size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t splits);
+
+// FP8 e4m3 block quantization of a bf16 [tokens][heads][head_dim] sequence
+// given as n_spans spans (end: exclusive prefix sums of their lengths) into
+// blocks of `rows` rows per head (rows = 64: key tiles in the attention
+// kernel's LDS layout; rows = 32: plain row-major query blocks).  head_dim 128.
+hipError_t launch_quant_e4m3(const void* const* src, const int32_t* end, int n_spans, int32_t tokens, int32_t heads,
+                             int head_dim, int rows, uint8_t* codes, float* scales, hipStream_t s);
 
 // fp32 attention (plain SIMT; correctness path for fp32 inputs).
 hipError_t launch_attn_f32(const AttnCall& c, hipStream_t s);

@@ -440,3 +440,64 @@ def test_retained_argument_errors(lib, dry):
     assert _attn_keep(lib, h, 0, [], hd, 40, seg) == wmk.WMK_OK      # segments only
     assert _spans(dry) == [(40, QBUF, SBUF)]
     lib.wmk_cache_destroy(h)
+
+
+def _qk8(lib, h, hd, nq, segs, ws, wsb, layer=0, scale=0.088):
+    arr = (wmk.wmk_kv_segment * max(1, len(segs)))(*[wmk.wmk_kv_segment(k, v, t) for k, v, t in segs])
+    return lib.wmk_chunk_attention_qk8(h, layer, ctypes.byref(hd), QBUF, nq, arr, len(segs), OBUF, scale, ws, wsb,
+                                       None)
+
+
+def _qk8_layout(H, nq, nk):
+    a = lambda x: (x + 255) // 256 * 256
+    kt, qb = -(-nk // 64), -(-nq // 32)
+    return a(kt * H * 8192) + a(kt * H * 4) + a(qb * H * 4096) + a(qb * H * 4)
+
+
+def test_qk8_workspace_errors_and_plan(lib, dry):
+    """FP8 QK^T: the workspace holds the quantized operands (sized from the key count) and
+    is required; the rest of it serves the split tail as for the plain call."""
+    d = _desc()
+    _, h = _init(lib, d)
+    for _ in range(4):
+        assert lib.wmk_cache_append_evict(h, 0, QBUF, SBUF, 4, None) == wmk.WMK_OK
+    hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
+    nk = 14 * 1508 + 6032
+    need = _qk8_layout(12, 6032, nk)
+    full = lib.wmk_attention_qk8_workspace_bytes(ctypes.byref(hd), 6032, nk)
+    assert full == need + lib.wmk_attention_workspace_bytes(ctypes.byref(hd), 6032)
+    for bad_hd in (wmk.wmk_head_desc(12, 64, wmk.WMK_BF16), wmk.wmk_head_desc(12, 128, wmk.WMK_F32)):
+        assert lib.wmk_attention_qk8_workspace_bytes(ctypes.byref(bad_hd), 6032, nk) == 0
+    cur = [(QBUF, SBUF, 6032)]
+    WS = 0x60000000
+    bad = [
+        (dict(ws=None, wsb=0), wmk.WMK_ERR_CAPACITY),
+        (dict(ws=WS, wsb=need - 1), wmk.WMK_ERR_CAPACITY),
+        (dict(ws=WS + 16, wsb=need), wmk.WMK_ERR_ALIGN),
+        (dict(hd=wmk.wmk_head_desc(12, 128, wmk.WMK_F32)), wmk.WMK_ERR_DTYPE),
+        (dict(segs=[(QBUF, SBUF, 8)] * 5), wmk.WMK_ERR_SHAPE),
+        (dict(layer=3), wmk.WMK_ERR_RANGE),
+        (dict(scale=0.0), wmk.WMK_ERR_RANGE),
+    ]
+    for kw, status in bad:
+        args = dict(hd=hd, segs=cur, ws=WS, wsb=need, layer=0, scale=0.088)
+        args.update(kw)
+        n_before = len(dry.read_text().splitlines()) if dry.exists() else 0
+        st = _qk8(lib, h, args["hd"], 6032, args["segs"], args["ws"], args["wsb"], layer=args["layer"],
+                  scale=args["scale"])
+        assert st == status, (kw, st)
+        assert (len(dry.read_text().splitlines()) if dry.exists() else 0) == n_before
+    # head_dim 64 is refused (a cache-less call with a 64-dim descriptor)
+    hd64 = wmk.wmk_head_desc(12, 64, wmk.WMK_BF16)
+    assert _qk8(lib, None, hd64, 100, [(QBUF, SBUF, 100)], WS, need) == wmk.WMK_ERR_SHAPE
+    # exactly the operand regions: planned as FP8, no split; the full size: split as the plain call
+    assert _qk8(lib, h, hd, 6032, cur, WS, need) == wmk.WMK_OK
+    p = _last_attn(dry)
+    assert (p["qk8"], p["kv"], p["split_units"]) == ("1", str(nk), "0")
+    assert _qk8(lib, h, hd, 6032, cur, WS, full) == wmk.WMK_OK
+    p = _last_attn(dry)
+    assert _attn(lib, h, 0, hd, 6032, cur, ws=WS, wsb=full - need) == wmk.WMK_OK
+    q = _last_attn(dry)
+    assert q["qk8"] == "0" and (p["split_units"], p["splits"]) == (q["split_units"], q["splits"])
+    assert int(p["split_units"]) > 0
+    lib.wmk_cache_destroy(h)
