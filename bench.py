@@ -39,7 +39,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--skip-extra", action="store_true", help="skip the MoBA and 720p workloads")
+    ap.add_argument("--skip-extra", action="store_true", help="skip the other workloads (same as --extra none)")
+    ap.add_argument("--extra", default="all",
+                    help="other workloads to run, comma separated: moba, 720p, qk8, retained, rolling, cross_train "
+                         "(or all, none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -200,8 +203,10 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 2 * n
 
-    if not args.skip_extra:
-        result["other_workloads"] = other_workloads(wmk, synth, torch, np, fill, dev, stream, reps=5)
+    extra = set() if args.skip_extra or args.extra == "none" else (
+        {"moba", "720p", "qk8", "retained", "rolling", "cross_train"} if args.extra == "all" else set(args.extra.split(",")))
+    if extra:
+        result["other_workloads"] = other_workloads(wmk, synth, torch, np, fill, dev, stream, reps=5, which=extra)
 
     del cache, kfin, vfin, q, k, v, out
     torch.cuda.empty_cache()
@@ -210,7 +215,7 @@ def main():
     print(json.dumps(result))
 
 
-def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps):
+def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps, which):
     res = {}
 
     def timed(fn):
@@ -226,122 +231,151 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps):
             ms.append(a.elapsed_time(b))
         return float(np.mean(ms)), float(np.min(ms))
 
-    # MoBA training sequence: 21 clean + 21 noisy + 21 block frames of 1560 tokens, chunks of 3
-    tpf, frames, cf = 1560, 21, 3
-    n = 3 * frames * tpf
-    mq, mk, mv = (fill((n, H, D), kind=t) for t in (synth.Q, synth.K, synth.V))
-    mo = torch.empty_like(mq)
-    pairs = 945 * tpf * tpf
-    mflops = 4.0 * D * H * pairs
-    avg, mn = timed(lambda: wmk.moba_attention(mq, mk, mv, tokens_per_frame=tpf, frames=frames, chunk_frames=cf,
-                                               out=mo))
-    res["moba_98280"] = {"ms_avg": round(avg, 3), "ms_min": round(mn, 3), "tflops": round(mflops / avg / 1e9, 1),
-                         "frac_peak": round(mflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
-                         "allowed_pairs_per_head": pairs, "dense_fraction": round(945 / 3969, 4)}
-    del mq, mk, mv, mo
+    if "moba" in which:
+        # MoBA training sequence: 21 clean + 21 noisy + 21 block frames of 1560 tokens, chunks of 3
+        tpf, frames, cf = 1560, 21, 3
+        n = 3 * frames * tpf
+        mq, mk, mv = (fill((n, H, D), kind=t) for t in (synth.Q, synth.K, synth.V))
+        mo = torch.empty_like(mq)
+        pairs = 945 * tpf * tpf
+        mflops = 4.0 * D * H * pairs
+        avg, mn = timed(lambda: wmk.moba_attention(mq, mk, mv, tokens_per_frame=tpf, frames=frames, chunk_frames=cf,
+                                                   out=mo))
+        res["moba_98280"] = {"ms_avg": round(avg, 3), "ms_min": round(mn, 3), "tflops": round(mflops / avg / 1e9, 1),
+                             "frac_peak": round(mflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                             "allowed_pairs_per_head": pairs, "dense_fraction": round(945 / 3969, 4)}
+        del mq, mk, mv, mo
 
-    # 720p step: 3600 tokens per frame, 24 heads, 18 slots; chunk-causal cross-attention
-    tpf, heads = 3600, 24
-    c = wmk.Cache(num_layers=1, num_heads=heads, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
-                  chunk_frames=CF)
-    nq = CF * tpf
-    for i in range(4):
-        kf = fill((nq, heads, D), chunk=i, step=4, kind=synth.KFIN)
-        vf = fill((nq, heads, D), chunk=i, step=4, kind=synth.VFIN)
-        c.append_evict(0, kf, vf, CF)
-    q, k, v = (fill((nq, heads, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
-    o = torch.empty_like(q)
-    kv = (S + W + CF) * tpf
-    sflops = 4.0 * D * heads * nq * kv
-    avg, mn = timed(lambda: wmk.chunk_attention(c, 0, q, [(k, v)], out=o))
-    res["720p_self"] = {"ms_avg": round(avg, 3), "ms_min": round(mn, 3), "tflops": round(sflops / avg / 1e9, 1),
-                        "frac_peak": round(sflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4), "q_tokens": nq,
-                        "kv_tokens": kv}
-    ab = 2.0 * 2 * nq * heads * D * 2
-    avg_a, mn_a = timed(lambda: c.append_evict(0, kf, vf, CF))
-    res["720p_append_evict"] = {"us_avg": round(avg_a * 1e3, 1), "GBps": round(ab / avg_a / 1e6, 1),
-                                "frac_hbm": round(ab / avg_a / 1e6 / PEAK_HBM_GBPS, 4)}
-    ke, ve = fill((512, heads, D), kind=synth.KENV), fill((512, heads, D), kind=synth.VENV)
-    kl, vl = fill((512, heads, D), chunk=2, kind=synth.KLOC), fill((512, heads, D), chunk=2, kind=synth.VLOC)
-    cflops = 4.0 * D * heads * nq * 1024
-    avg, mn = timed(lambda: wmk.chunk_attention(None, 0, q, [(ke, ve), (kl, vl)], out=o))
-    res["720p_cross"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(cflops / avg / 1e9, 1),
-                         "frac_peak": round(cflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
-    del c, q, k, v, o
-    torch.cuda.empty_cache()
+    if "720p" in which:
+        # 720p step: 3600 tokens per frame, 24 heads, 18 slots; chunk-causal cross-attention
+        tpf, heads = 3600, 24
+        c = wmk.Cache(num_layers=1, num_heads=heads, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=CF)
+        nq = CF * tpf
+        for i in range(4):
+            kf = fill((nq, heads, D), chunk=i, step=4, kind=synth.KFIN)
+            vf = fill((nq, heads, D), chunk=i, step=4, kind=synth.VFIN)
+            c.append_evict(0, kf, vf, CF)
+        q, k, v = (fill((nq, heads, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
+        o = torch.empty_like(q)
+        kv = (S + W + CF) * tpf
+        sflops = 4.0 * D * heads * nq * kv
+        avg, mn = timed(lambda: wmk.chunk_attention(c, 0, q, [(k, v)], out=o))
+        res["720p_self"] = {"ms_avg": round(avg, 3), "ms_min": round(mn, 3), "tflops": round(sflops / avg / 1e9, 1),
+                            "frac_peak": round(sflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4), "q_tokens": nq,
+                            "kv_tokens": kv}
+        ab = 2.0 * 2 * nq * heads * D * 2
+        avg_a, mn_a = timed(lambda: c.append_evict(0, kf, vf, CF))
+        res["720p_append_evict"] = {"us_avg": round(avg_a * 1e3, 1), "GBps": round(ab / avg_a / 1e6, 1),
+                                    "frac_hbm": round(ab / avg_a / 1e6 / PEAK_HBM_GBPS, 4)}
+        ke, ve = fill((512, heads, D), kind=synth.KENV), fill((512, heads, D), kind=synth.VENV)
+        kl, vl = fill((512, heads, D), chunk=2, kind=synth.KLOC), fill((512, heads, D), chunk=2, kind=synth.VLOC)
+        cflops = 4.0 * D * heads * nq * 1024
+        avg, mn = timed(lambda: wmk.chunk_attention(None, 0, q, [(ke, ve), (kl, vl)], out=o))
+        res["720p_cross"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(cflops / avg / 1e9, 1),
+                             "frac_peak": round(cflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4)}
+        del c, q, k, v, o
+        torch.cuda.empty_cache()
 
-    # FP8-quantized QK^T at 832x464: warm cache + the current chunk; one call =
-    # quantization of Q and of the key sequence, then the attention kernel
-    c8 = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S, window_frames=W,
-                   chunk_frames=CF)
-    nq8 = CF * TPF
-    for i in range(4):
-        c8.append_evict(0, fill((nq8, H, D), chunk=i, step=4, kind=synth.KFIN),
-                        fill((nq8, H, D), chunk=i, step=4, kind=synth.VFIN), CF)
-    q8, k8, v8 = (fill((nq8, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
-    o8 = torch.empty_like(q8)
-    f8 = 4.0 * D * H * nq8 * (S + W + CF) * TPF
-    avg, mn = timed(lambda: wmk.chunk_attention_qk8(c8, 0, q8, [(k8, v8)], out=o8))
-    res["832x464_qk8"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(f8 / avg / 1e9, 1),
-                          "frac_peak_bf16": round(f8 / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
-                          "note": "QK^T in fp8 e4m3 (per-block scales, quantization passes included), P V in bf16"}
-    del c8, q8, k8, v8, o8
-    torch.cuda.empty_cache()
+    if "qk8" in which:
+        # FP8-quantized QK^T at 832x464: warm cache + the current chunk; one call =
+        # quantization of Q and of the key sequence, then the attention kernel
+        c8 = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S, window_frames=W,
+                       chunk_frames=CF)
+        nq8 = CF * TPF
+        for i in range(4):
+            c8.append_evict(0, fill((nq8, H, D), chunk=i, step=4, kind=synth.KFIN),
+                            fill((nq8, H, D), chunk=i, step=4, kind=synth.VFIN), CF)
+        q8, k8, v8 = (fill((nq8, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
+        o8 = torch.empty_like(q8)
+        f8 = 4.0 * D * H * nq8 * (S + W + CF) * TPF
+        avg, mn = timed(lambda: wmk.chunk_attention_qk8(c8, 0, q8, [(k8, v8)], out=o8))
+        res["832x464_qk8"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4), "tflops": round(f8 / avg / 1e9, 1),
+                              "frac_peak_bf16": round(f8 / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                              "note": "QK^T in fp8 e4m3 (per-block scales, quantization passes included), P V in bf16"}
+        del c8, q8, k8, v8, o8
+        torch.cuda.empty_cache()
 
-    # rolling session at 832x464: 30 layers x 4 denoising steps per chunk over a
-    # full 18-slot cache, then the finalized chunk appended to every layer
-    layers, steps = 30, 4
-    nq = CF * TPF
-    rc = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
-                   window_frames=W, chunk_frames=CF)
-    pool = [tuple(fill((nq, H, D), chunk=i, kind=t) for t in (synth.Q, synth.K, synth.V)) for i in range(2)]
-    fin = [tuple(fill((nq, H, D), chunk=i, step=4, kind=t) for t in (synth.KFIN, synth.VFIN)) for i in range(2)]
-    ro = torch.empty((nq, H, D), dtype=torch.bfloat16, device=dev)
+    if "retained" in which:
+        # variable retention at 832x464: of the 14 resident frames keep the 6 anchors and
+        # the 4 most recent (in 3 runs of adjacent slots after the ring wrapped) + the chunk
+        cr = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S, window_frames=W,
+                       chunk_frames=CF)
+        nqr = CF * TPF
+        for i in range(5):
+            cr.append_evict(0, fill((nqr, H, D), chunk=i, step=4, kind=synth.KFIN),
+                            fill((nqr, H, D), chunk=i, step=4, kind=synth.VFIN), CF)
+        slots_r, _ = cr.slots(0)
+        keep = sorted(f for f in slots_r if f >= 0)
+        keep = keep[:S] + keep[-4:]
+        qr, kr, vr = (fill((nqr, H, D), chunk=5, kind=t) for t in (synth.Q, synth.K, synth.V))
+        orr = torch.empty_like(qr)
+        fr = 4.0 * D * H * nqr * (len(keep) * TPF + nqr)
+        avg, mn = timed(lambda: wmk.chunk_attention(cr, 0, qr, [(kr, vr)], out=orr, keep_frames=keep))
+        res["832x464_retained_10_of_14"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4),
+                                            "tflops": round(fr / avg / 1e9, 1),
+                                            "frac_peak": round(fr / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                            "kv_tokens": len(keep) * TPF + nqr, "kept_frames": keep}
+        del cr, qr, kr, vr, orr
+        torch.cuda.empty_cache()
 
-    def chunk(ci):
-        for st in range(steps):
+    if "rolling" in which:
+        # rolling session at 832x464: 30 layers x 4 denoising steps per chunk over a
+        # full 18-slot cache, then the finalized chunk appended to every layer
+        layers, steps = 30, 4
+        nq = CF * TPF
+        rc = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
+                       window_frames=W, chunk_frames=CF)
+        pool = [tuple(fill((nq, H, D), chunk=i, kind=t) for t in (synth.Q, synth.K, synth.V)) for i in range(2)]
+        fin = [tuple(fill((nq, H, D), chunk=i, step=4, kind=t) for t in (synth.KFIN, synth.VFIN)) for i in range(2)]
+        ro = torch.empty((nq, H, D), dtype=torch.bfloat16, device=dev)
+
+        def chunk(ci):
+            for st in range(steps):
+                for l in range(layers):
+                    rq, rk, rv = pool[(st + l) % 2]
+                    wmk.chunk_attention(rc, l, rq, [(rk, rv)], out=ro)
             for l in range(layers):
-                rq, rk, rv = pool[(st + l) % 2]
-                wmk.chunk_attention(rc, l, rq, [(rk, rv)], out=ro)
-        for l in range(layers):
-            rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
+                rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
 
-    for ci in range(4):  # warm the cache to 14 resident frames
-        for l in range(layers):
-            rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
-    chunk(4)
-    torch.cuda.synchronize()
-    n_chunks = 3
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for ci in range(n_chunks):
-        chunk(5 + ci)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    per_chunk = e0.elapsed_time(e1) / n_chunks
-    chunk_flops = layers * steps * 4.0 * D * H * nq * (S + W + CF) * TPF
-    res["rolling_832x464_steady_chunk"] = {
-        "ms_per_chunk": round(per_chunk, 2), "calls_per_chunk": layers * steps, "appends_per_chunk": layers,
-        "tflops": round(chunk_flops / per_chunk / 1e9, 1),
-        "ms_per_60_chunk_session_at_steady_rate": round(60 * per_chunk, 1)}
-    del rc, pool, fin, ro
-    torch.cuda.empty_cache()
+        for ci in range(4):  # warm the cache to 14 resident frames
+            for l in range(layers):
+                rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
+        chunk(4)
+        torch.cuda.synchronize()
+        n_chunks = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for ci in range(n_chunks):
+            chunk(5 + ci)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_chunk = e0.elapsed_time(e1) / n_chunks
+        chunk_flops = layers * steps * 4.0 * D * H * nq * (S + W + CF) * TPF
+        res["rolling_832x464_steady_chunk"] = {
+            "ms_per_chunk": round(per_chunk, 2), "calls_per_chunk": layers * steps, "appends_per_chunk": layers,
+            "tflops": round(chunk_flops / per_chunk / 1e9, 1),
+            "ms_per_60_chunk_session_at_steady_rate": round(60 * per_chunk, 1)}
+        del rc, pool, fin, ro
+        torch.cuda.empty_cache()
 
-    # chunk-causal cross-attention over a training sequence: the MoBA shape's 7
-    # chunks of 3 frames x 1560 tokens, each reading a 512-token environment
-    # prompt and its own 512-token local prompt (12 heads)
-    tpf, heads, cq, nc, ne, nl = 1560, 12, 3 * 1560, 7, 512, 512
-    q = fill((cq * nc, heads, D), kind=synth.Q)
-    kx = fill((ne + nc * nl, heads, D), kind=synth.KLOC)
-    vx = fill((ne + nc * nl, heads, D), kind=synth.VLOC)
-    o = torch.empty_like(q)
-    xflops = 4.0 * D * heads * cq * nc * (ne + nl)
-    avg, mn = timed(lambda: wmk.cross_attention_train(q, kx, vx, chunk_q_tokens=cq, env_tokens=ne, local_tokens=nl,
-                                                      out=o))
-    res["cross_train_32760"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4),
-                                "tflops": round(xflops / avg / 1e9, 1),
-                                "frac_peak": round(xflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
-                                "q_tokens": cq * nc, "kv_tokens": ne + nc * nl}
+    if "cross_train" in which:
+        # chunk-causal cross-attention over a training sequence: the MoBA shape's 7
+        # chunks of 3 frames x 1560 tokens, each reading a 512-token environment
+        # prompt and its own 512-token local prompt (12 heads)
+        tpf, heads, cq, nc, ne, nl = 1560, 12, 3 * 1560, 7, 512, 512
+        q = fill((cq * nc, heads, D), kind=synth.Q)
+        kx = fill((ne + nc * nl, heads, D), kind=synth.KLOC)
+        vx = fill((ne + nc * nl, heads, D), kind=synth.VLOC)
+        o = torch.empty_like(q)
+        xflops = 4.0 * D * heads * cq * nc * (ne + nl)
+        avg, mn = timed(lambda: wmk.cross_attention_train(q, kx, vx, chunk_q_tokens=cq, env_tokens=ne, local_tokens=nl,
+                                                          out=o))
+        res["cross_train_32760"] = {"ms_avg": round(avg, 4), "ms_min": round(mn, 4),
+                                    "tflops": round(xflops / avg / 1e9, 1),
+                                    "frac_peak": round(xflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
+                                    "q_tokens": cq * nc, "kv_tokens": ne + nc * nl}
+
     return res
 
 
