@@ -459,3 +459,69 @@ def chunk_attention_qk8(cache, q, segments, scale, rows=None):
     if rows is not None:
         qd = qd[np.asarray(rows)]
     return attend_dense_f64(qd, kd, v_all, scale)
+
+
+# --------------------------------------------------------------------------------------------
+# MoBA backward: gradients of the masked attention w.r.t. q, k, v (the training use of the MoBA
+# mask, "Infinite Worlds with Versatile Interactions", causal pretraining paragraph).  The pages
+# state no backward; this is the derivative of the forward above, written out per head:
+#   S = scale Q K^T (masked entries -inf),  P = softmax_rows(S) (an empty row is 0),  O = P V,
+#   dV = P^T dO,  dP = dO V^T,  D_i = sum_d dO_id O_id,  dS = P * (dP - D),
+#   dQ = scale dS K,  dK = scale dS^T Q.
+# The forward for training also returns lse_i = log sum_j exp(S_ij) (natural log; -inf for a
+# row with no key).
+# --------------------------------------------------------------------------------------------
+
+def mask_from_row_intervals(intervals, nk):
+    """Dense boolean mask [nq][nk] from per-row lists of half-open key ranges."""
+    m = np.zeros((len(intervals), nk), dtype=bool)
+    for i, ivs in enumerate(intervals):
+        for a, b in ivs:
+            m[i, a:b] = True
+    return m
+
+
+def attention_lse(q, k, mask, scale):
+    """lse [H][nq] (fp64) of the masked scores: log sum_j exp(scale q_i . k_j) over allowed j."""
+    q = widen(q).astype(np.float64)
+    k = widen(k).astype(np.float64)
+    out = np.empty((q.shape[1], q.shape[0]), np.float64)
+    for hh in range(q.shape[1]):
+        s = np.where(mask, (q[:, hh, :] @ k[:, hh, :].T) * scale, -np.inf)
+        mx = s.max(axis=1)
+        safe = np.where(np.isfinite(mx), mx, 0.0)
+        out[hh] = safe + np.log(np.exp(s - safe[:, None]).sum(axis=1))
+    return out
+
+
+def attention_backward(q, k, v, dout, mask, scale):
+    """(dq, dk, dv), each fp64 with the shape of its input, of L = sum(dout * O) for the
+    masked attention O = softmax(scale q k^T) v, dense per head."""
+    q, k, v, do = (widen(x).astype(np.float64) for x in (q, k, v, dout))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for hh in range(q.shape[1]):
+        Q, K, V, dO = q[:, hh, :], k[:, hh, :], v[:, hh, :], do[:, hh, :]
+        s = np.where(mask, (Q @ K.T) * scale, -np.inf)
+        mx = s.max(axis=1, keepdims=True)
+        e = np.exp(s - np.where(np.isfinite(mx), mx, 0.0))
+        den = e.sum(axis=1, keepdims=True)
+        p = np.divide(e, den, out=np.zeros_like(e), where=den > 0)
+        o = p @ V
+        dv[:, hh, :] = p.T @ dO
+        dp = dO @ V.T
+        dsum = (dO * o).sum(axis=1, keepdims=True)
+        ds = p * (dp - dsum)
+        dq[:, hh, :] = scale * (ds @ K)
+        dk[:, hh, :] = scale * (ds.T @ Q)
+    return dq, dk, dv
+
+
+def moba_mask(tokens_per_frame, frames, chunk_frames, bidir_block=1):
+    n = (2 + bidir_block) * frames * tokens_per_frame
+    ivs = [moba_row_intervals(i, tokens_per_frame, frames, chunk_frames, bidir_block) for i in range(n)]
+    return mask_from_row_intervals(ivs, n)
+
+
+def moba_attention_backward(q, k, v, dout, tokens_per_frame, frames, chunk_frames, bidir_block, scale):
+    """Gradients of the MoBA-masked attention (dense; for sequences the oracle holds whole)."""
+    return attention_backward(q, k, v, dout, moba_mask(tokens_per_frame, frames, chunk_frames, bidir_block), scale)

@@ -817,3 +817,64 @@ def test_qk8_error_against_exact_attention_is_small():
 # 3 mantissa bits, so each score carries an error of a few percent of its magnitude
 QK8_REL_L2_VS_EXACT = 0.1
 QK8_MAX_ABS_VS_EXACT = 0.05
+
+
+# ---------------------------------------------------------------------------------------------
+# MoBA backward: gradients against central finite differences of the forward (C fp64 core)
+# ---------------------------------------------------------------------------------------------
+
+def _grid(shape, seed):
+    """Values on a 2^-10 grid in (-4, 4): q +- 2^-12 stays exact in fp32."""
+    rng = np.random.default_rng(seed)
+    return (np.round(rng.standard_normal(shape) * 1024) / 1024).clip(-3.9, 3.9).astype(np.float32)
+
+
+@pytest.mark.parametrize("tpf,frames,cf,bidir", [(2, 3, 1, 1), (1, 4, 2, 0), (3, 2, 1, 1)])
+def test_moba_backward_matches_finite_differences(tpf, frames, cf, bidir):
+    H, D, scale, h = 2, 8, 0.35, 2.0 ** -12
+    n = (2 + bidir) * frames * tpf
+    q, k, v = _grid((n, H, D), 1), _grid((n, H, D), 2), _grid((n, H, D), 3)
+    do = _rand((n, H, D), 4).astype(np.float64)
+    ivs = [oracle.moba_row_intervals(i, tpf, frames, cf, bidir) for i in range(n)]
+
+    def loss(qq, kk, vv):
+        return float((oracle.attend(qq, kk, vv, ivs, scale) * do).sum())
+
+    dq, dk, dv = oracle.moba_attention_backward(q, k, v, do.astype(np.float32), tpf, frames, cf, bidir, scale)
+    do = do.astype(np.float32).astype(np.float64)       # the gradients were taken for the fp32 dO
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros(x.shape)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=2e-6 * max(1.0, np.abs(fd).max()), err_msg=name)
+
+
+def test_backward_identities_and_empty_rows():
+    """Softmax is invariant to a shift of all of a row's keys (sum_j dK_j = 0) and its rows sum
+    to one (sum_j dV_j = sum of dO over rows that have keys); a row with no key gets dq = 0."""
+    n, H, D = 12, 2, 16
+    q, k, v, do = (_rand((n, H, D), 50 + i) for i in range(4))
+    mask = np.tril(np.ones((n, n), bool))
+    mask[5] = False                                       # row 5 sees nothing
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, mask, 0.25)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    has = mask.any(axis=1)
+    np.testing.assert_allclose(dv.sum(axis=0), do[has].astype(np.float64).sum(axis=0), atol=1e-12)
+    assert not dq[5].any()
+
+
+def test_lse_matches_c_probabilities():
+    n, H, D = 10, 2, 16
+    q, k = _rand((n, H, D), 60), _rand((n, H, D), 61)
+    ivs = [oracle.moba_row_intervals(i, 2, 5, 2, 0) for i in range(n)]
+    mask = oracle.mask_from_row_intervals(ivs, n)
+    lse = oracle.attention_lse(q, k, mask, 0.3)
+    _, probs = oracle.attend(q, k, np.zeros_like(k), ivs, 0.3, want_probs=True)   # [nq][H][nk]
+    s = np.einsum("ihd,jhd->hij", q.astype(np.float64), k.astype(np.float64)) * 0.3
+    p = np.where(mask[None], np.exp(s - lse[:, :, None]), 0.0)
+    np.testing.assert_allclose(p.transpose(1, 0, 2), probs, atol=1e-14)
