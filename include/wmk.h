@@ -234,6 +234,38 @@ wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, c
                               const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* MoBA forward for training: wmk_moba_attention plus the per-row log-sum-exp
+ * the backward needs.  lse is [num_heads][n] fp32 (n = sequence length), lse =
+ * log sum_j exp(scale q_i . k_j) over the keys row i is allowed (natural log;
+ * -inf for a row with none).  bf16 only.  Errors as wmk_moba_attention, plus
+ * NULL lse -> WMK_ERR_NULL, misaligned lse -> WMK_ERR_ALIGN, dtype not bf16
+ * -> WMK_ERR_DTYPE. */
+wmk_status wmk_moba_attention_train(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
+                                    const void* v, void* out, float* lse, float scale, hipStream_t stream);
+
+/* Workspace bytes of wmk_moba_attention_backward (one fp32 per row and head);
+ * 0 for an invalid descriptor. */
+size_t wmk_moba_backward_workspace_bytes(const wmk_moba_desc* m, const wmk_head_desc* hd);
+
+/* MoBA backward: the gradients dq, dk, dv of L = sum(dout * out) for out =
+ * wmk_moba_attention(q, k, v) under the same mask (the training use of the
+ * MoBA mask, "Infinite Worlds with Versatile Interactions", causal
+ * pretraining paragraph), with the same skip of tiles no row allows.  With
+ * P = exp(scale q k^T - lse) on allowed pairs, D_i = dout_i . out_i:
+ * dv = P^T dout, dS = P (dout v^T - D), dq = scale dS k, dk = scale dS^T q.
+ * out and lse are those of wmk_moba_attention_train on the same inputs.
+ * q, k, v, out, dout, dq, dk, dv: [n][num_heads][128] bf16; the gradients
+ * must not overlap the inputs.  workspace: at least
+ * wmk_moba_backward_workspace_bytes (16-byte aligned), overwritten.
+ * Errors as wmk_moba_attention, plus NULL dout/lse/dq/dk/dv -> WMK_ERR_NULL,
+ * dtype not bf16 -> WMK_ERR_DTYPE, head_dim not 128 -> WMK_ERR_SHAPE,
+ * misaligned -> WMK_ERR_ALIGN, workspace NULL or too small ->
+ * WMK_ERR_CAPACITY. */
+wmk_status wmk_moba_attention_backward(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
+                                       const void* v, const void* out, const void* dout, const float* lse, void* dq,
+                                       void* dk, void* dv, float scale, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 /* Chunk-causal cross-attention forward over a multi-chunk sequence (the
  * training form of the chunk-wise prompt conditioning: "Infinite Worlds with
  * Versatile Interactions", causal pretraining paragraph -- a causal

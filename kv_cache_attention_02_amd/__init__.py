@@ -72,6 +72,13 @@ _SIGNATURES = {
                                                     ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "wmk_moba_attention": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P, _P, _P,
                                           _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "wmk_moba_attention_train": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P,
+                                                _P, _P, _P, _P, ctypes.c_float, _P]),
+    "wmk_moba_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_moba_desc),
+                                                            ctypes.POINTER(wmk_head_desc)]),
+    "wmk_moba_attention_backward": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P,
+                                                   _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P,
+                                                   ctypes.c_size_t, _P]),
     "wmk_cross_attention_train": (ctypes.c_int, [ctypes.POINTER(wmk_xattn_desc), ctypes.POINTER(wmk_head_desc), _P,
                                                  _P, _P, _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "wmk_last_error": (ctypes.c_char_p, []),
@@ -290,6 +297,40 @@ def moba_attention(q, k, v, *, tokens_per_frame, frames, chunk_frames, bidir_blo
     _check(load().wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                      scale, None, 0, _stream_ptr(stream)))
     return out
+
+
+def moba_attention_train(q, k, v, *, tokens_per_frame, frames, chunk_frames, bidir_block=1, out=None, lse=None,
+                         scale=None, stream=None):
+    """MoBA forward for training: returns (out, lse) with lse [H][n] fp32 (natural log)."""
+    torch = _torch()
+    n, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, n), dtype=torch.float32, device=q.device)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    md = wmk_moba_desc(tokens_per_frame, frames, chunk_frames, bidir_block)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(load().wmk_moba_attention_train(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                           _ptr(lse), scale, _stream_ptr(stream)))
+    return out, lse
+
+
+def moba_attention_backward(q, k, v, out, dout, lse, *, tokens_per_frame, frames, chunk_frames, bidir_block=1,
+                            scale=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(dout * out) for the MoBA-masked attention."""
+    torch = _torch()
+    n, H, D = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    md = wmk_moba_desc(tokens_per_frame, frames, chunk_frames, bidir_block)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    wsb = load().wmk_moba_backward_workspace_bytes(ctypes.byref(md), ctypes.byref(hd))
+    ws = workspace(q.device, wsb)
+    _check(load().wmk_moba_attention_backward(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), scale,
+                                              _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return dq, dk, dv
 
 
 def cross_attention_train(q, k, v, *, chunk_q_tokens, env_tokens, local_tokens, out=None, scale=None,

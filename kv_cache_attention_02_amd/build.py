@@ -5,7 +5,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["wmk_api.cpp", "attn_bf16.hip", "attn_f32.hip", "cache_append.hip", "quant_fp8.hip"]
+SOURCES = ["wmk_api.cpp", "attn_bf16.hip", "attn_f32.hip", "cache_append.hip", "quant_fp8.hip", "attn_bwd.hip"]
 LIB = os.path.join(PKG, "libwmk.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,550 @@
+// Backward of the MoBA-masked attention (bf16, head_dim 128) on the CDNA4
+// matrix cores: dQ, dK, dV of L = sum(dO * O) for O = softmax(scale Q K^T) V
+// under the MoBA mask ("Infinite Worlds with Versatile Interactions", causal
+// pretraining paragraph; "Mix Forcing", "Mix the training modes"), with the
+// same per-tile skip as the forward: only tiles some row (or column) of a
+// workgroup allows are visited.
+//
+// With the forward's log-sum-exp (lse) and D_i = dO_i . O_i, per head:
+//   P = exp(scale Q K^T - lse),  dP = dO V^T,  dS = P * (dP - D),
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+// Two kernels, each a loop over 64-row tiles staged in LDS by direct loads
+// (double buffered, one barrier per tile), 8 waves x 32 rows of their own:
+//   bwd_dq_kernel:   a workgroup owns 256 query rows and walks the key tiles
+//                    its rows allow.  S^T = K Q^T and dP^T = V dO^T (lane =
+//                    query, as in the forward), dS^T -> bf16, dQ^T += K^T dS^T
+//                    with K^T from transposing LDS reads.
+//   bwd_dkdv_kernel: a workgroup owns 256 keys and walks the query tiles that
+//                    allow them.  S = Q K^T and dP = dO V^T (lane = key), P and
+//                    dS -> bf16, dV^T += dO^T P and dK^T += Q^T dS with dO^T,
+//                    Q^T from transposing LDS reads.
+// A prologue kernel forms D from dO and O.  Every MFMA is
+// v_mfma_f32_32x32x16_bf16; accumulators are fp32.
+//
+// LDS tiles are [64 rows][256 B], the 16-byte chunk c of row r stored at
+// c ^ (((r & 3) << 2) | ((r >> 2) & 3)): 16 consecutive rows at one logical
+// chunk hit 16 distinct chunk positions (row reads), and the 8 rows x 64 B of a
+// transposing read spread over all banks.
+#include <math.h>
+
+#include "attn_tiles.h"
+#include "wmk_internal.h"
+
+namespace wmk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int NW = 8;            // waves per workgroup
+constexpr int NT = NW * 64;      // threads per workgroup
+constexpr int HD = 128;          // head_dim
+constexpr int ROWB = HD * 2;     // bytes per row of one head
+constexpr int TR = 64;           // rows per LDS tile
+constexpr int TILEB = TR * ROWB; // 16 KB
+constexpr int BR = NW * 32;      // rows a workgroup owns
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// Per-lane LDS byte offsets of the fragment reads, fixed for the kernel (kept
+// few: the row-read offset of k-step ds is base + (xr ^ 32 ds), and the second
+// transposing read of a k-step sits at (tr0 ^ 32) + 8 rows, because
+// swz(r + 8) = swz(r) ^ 2 for r < 8).
+struct Frag {
+    uint32_t base;     // row read (A operand, row l32 of a 32-row block): row start + the chunk's low bit
+    uint32_t xr;       // (swz(l32) & 14) * 16: the chunk bits the k-step's chunk is XORed with
+    uint32_t tr0[4];   // transposing read, 32-dim block db, rows +0..7 of a 16-row k-step
+};
+
+__device__ __forceinline__ Frag frag_offsets(int lane) {
+    Frag f;
+    const int l32 = lane & 31, h = lane >> 5;
+    // chunk (2 ds + h) ^ swz = (2 ds ^ (swz & 14)) + ((h ^ swz) & 1)
+    f.base = (uint32_t)(l32 * ROWB + ((h ^ swz(l32)) & 1) * 16);
+    f.xr = (uint32_t)((swz(l32) & 14) * 16);
+    // in a 16-lane group, lane 4e+q names row 4hh+e (hh = g/2) at dims 4q..4q+3 of
+    // its 16-dim half g&1 (g = lane/16); the read hands lane i dim (i%4) of the
+    // rows of lanes i/4, i/4+4, ..: one dim (db*32 + lane%32) for 4 rows
+    const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3, hh = g >> 1;
+    const int r = 4 * hh + e;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int d = db * 32 + 16 * (g & 1) + 4 * q;
+        f.tr0[db] = (uint32_t)(r * ROWB + (((d >> 3) ^ swz(r)) * 16) + (d & 7) * 2);
+    }
+    return f;
+}
+
+// A operand from rows: rows 32 kb + l32, dims 16 ds + 8 h .. + 7
+__device__ __forceinline__ bf16x8 rows_frag(const char LDS_AS* tile, const Frag& f, int kb, int ds) {
+    return *(const bf16x8 LDS_AS*)(tile + kb * 32 * ROWB + f.base + (f.xr ^ (uint32_t)(32 * ds)));
+}
+
+// A operand transposed: dim 32 db + lane%32, the 8 rows 32 kb + 16 t + 8 u + 4 h + {0..3}
+// (u = 0, 1) -- the row order of registers 8t .. 8t+7 of a 32x32 accumulator
+__device__ __forceinline__ bf16x8 tr_frag(const char LDS_AS* tile, const Frag& f, int kb, int db, int t) {
+    const char LDS_AS* base = tile + (kb * 32 + 16 * t) * ROWB;
+    const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(base + f.tr0[db]));
+    const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(base + 8 * ROWB + (f.tr0[db] ^ 32u)));
+    const s16x8 v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, char LDS_AS* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void LDS_AS*)dst, 16, off, 0, 0, 0);
+}
+
+// Direct loads of rows [r0, r0 + 64) of one head of a [n][heads][128] bf16
+// tensor into an LDS tile (two 16-byte loads per thread); rows past n read 0.
+struct TileLoad {
+    uint32_t off[2];  // byte offset from the tile's first row of this head
+};
+__device__ __forceinline__ TileLoad tile_load_map(int tid, uint32_t row_stride) {
+    TileLoad m;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 32 * i + tid / 16, phys = tid % 16;
+        m.off[i] = (uint32_t)row * row_stride + (uint32_t)((phys ^ swz(row)) * 16);
+    }
+    return m;
+}
+__device__ __forceinline__ void load_tile(const char* src, int32_t r0, int32_t n, int32_t heads, int32_t head,
+                                          const TileLoad& m, char LDS_AS* tile, int wave) {
+    const uint32_t row_stride = (uint32_t)heads * ROWB;
+    const int32_t valid = max(0, min(TR, n - r0));
+    const __amdgpu_buffer_rsrc_t r = rsrc(src + ((size_t)r0 * heads + head) * ROWB, (uint32_t)valid * row_stride);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(r, m.off[i], tile + i * (TILEB / 2) + wave * 1024);
+}
+
+// Column view of the MoBA mask: the query rows that attend key j (at most two
+// ranges).  Transpose of tiles::row_ranges: clean key of chunk c -> clean rows
+// of chunks >= c and noisy rows of chunks > c; noisy key of chunk c -> noisy
+// rows of chunk c; block key -> block rows.
+__device__ __forceinline__ void col_ranges(const MaskShape& m, int32_t n, int32_t j, int32_t& lo0, int32_t& hi0,
+                                           int32_t& lo1, int32_t& hi1) {
+    lo0 = hi0 = lo1 = hi1 = 0;
+    if (j >= n) return;
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    const int32_t part = j / L, c = (j - part * L) / cl;
+    if (part == 0) {
+        lo0 = c * cl; hi0 = L;
+        lo1 = min(L + (c + 1) * cl, 2 * L); hi1 = m.parts > 1 ? 2 * L : lo1;
+    } else if (part == 1) {
+        lo0 = L + c * cl; hi0 = L + min((c + 1) * cl, L);
+    } else {
+        lo0 = 2 * L; hi0 = 3 * L;
+    }
+}
+
+// Union over keys [c0, c1) of their query ranges, in 64-row tiles (same form as
+// tiles::tile_ranges for rows).
+__device__ __forceinline__ tiles::TileRanges col_tile_ranges(const MaskShape& m, int32_t n, int32_t c0, int32_t c1) {
+    using namespace tiles;
+    int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    c1 = min(c1, n);
+    const int32_t pa = c0 / L, pb = (c1 - 1) / L;
+    if (c1 > c0) {
+        if (pa <= 0 && 0 <= pb) {  // clean keys: from the first key's chunk on, clean and (later) noisy rows
+            const int32_t ca = c0 / cl;
+            set_tiles(l0, h0, ca * cl, L);
+            if (m.parts > 1) set_tiles(l1, h1, min(L + (ca + 1) * cl, 2 * L), 2 * L);
+        }
+        if (pa <= 1 && 1 <= pb) {  // noisy keys: the noisy rows of their chunks
+            const int32_t fa = max(c0, L) - L, fb = min(c1, 2 * L) - L - 1;
+            set_tiles(l2, h2, L + (fa / cl) * cl, L + min((fb / cl + 1) * cl, L));
+        }
+        if (pa <= 2 && 2 <= pb) set_tiles(l3, h3, 2 * L, 3 * L);
+    }
+    return merge_ranges(l0, h0, l1, h1, l2, h2, l3, h3);
+}
+
+struct BwdArgs {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    const __bf16* dout;
+    const float* lse;   // [heads][n], natural log
+    const float* dsum;  // [heads][n], D = dO . O
+    __bf16* dq;
+    __bf16* dk;
+    __bf16* dv;
+    int32_t n;
+    int32_t heads;
+    float scale;
+    MaskShape mask;
+};
+
+// exp2 exponent offset of a row: lse in log2 units; a row with no key (lse =
+// -inf) gets +inf so that all its weights are 0
+__device__ __forceinline__ float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---- D_i = sum_d dO_id O_id per (row, head): 16 threads per row and head
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(const __bf16* dout, const __bf16* out, float* dsum, int32_t n,
+                                                       int32_t heads) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rh = gid / 16;  // row * heads + head
+    const int part = (int)(gid % 16);
+    float acc = 0.0f;
+    if (rh < (int64_t)n * heads) {
+        const u32x4 a = *(const u32x4*)(dout + rh * HD + part * 8);
+        const u32x4 b = *(const u32x4*)(out + rh * HD + part * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc += __uint_as_float(a[w] << 16) * __uint_as_float(b[w] << 16);
+            acc += __uint_as_float(a[w] & 0xffff0000u) * __uint_as_float(b[w] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    if (part == 0 && rh < (int64_t)n * heads) {
+        const int32_t row = (int32_t)(rh / heads), head = (int32_t)(rh % heads);
+        dsum[(size_t)head * n + row] = acc;
+    }
+}
+
+// workgroup -> (head, tile of BR rows); consecutive tiles of one head share an XCD
+__device__ __forceinline__ void unit_of(int32_t b, int32_t units, int32_t n_tiles, int32_t& head, int32_t& t) {
+    const int32_t x = b % kNumXcd, j = b / kNumXcd;
+    const int32_t per = units / kNumXcd, rem = units % kNumXcd;
+    const int32_t u = x * per + min(x, rem) + j;  // XCD x runs units [x per + min(x, rem), ...)
+    head = u / n_tiles;
+    t = u % n_tiles;
+}
+
+// ---- dQ: a workgroup owns BR query rows of one head
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char k0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char k1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char v0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char v1[TILEB];
+    const int32_t n_tiles = (a.n + BR - 1) / BR;
+    int32_t head, qt;
+    unit_of(blockIdx.x, n_tiles * a.heads, n_tiles, head, qt);
+    const int32_t r0 = qt * BR, r1 = min(r0 + BR, a.n);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int32_t row = r0 + wave * 32 + l32;
+    const bool row_ok = row < a.n;
+    const bool wave_has_rows = r0 + wave * 32 < a.n;
+
+    AttnCallN<1> rc{};  // row-interval view of the mask for tiles::row_ranges / tile_ranges
+    rc.q_tokens = a.n;
+    rc.kv_total = a.n;
+    rc.mask = a.mask;
+    const tiles::TileRanges tr = tiles::tile_ranges(rc, r0, r1);
+    int32_t lo0, hi0, lo1, hi1;
+    tiles::row_ranges(rc, row, lo0, hi0, lo1, hi1);
+
+    const int64_t stride = (int64_t)a.heads * HD;
+    bf16x8 qf[8], df[8];
+    {
+        const __bf16* qp = a.q + (int64_t)row * stride + (int64_t)head * HD + h * 8;
+        const __bf16* dp = a.dout + (int64_t)row * stride + (int64_t)head * HD + h * 8;
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+            qf[ds] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(qp + ds * 16) : u32x4{0u, 0u, 0u, 0u});
+            df[ds] = __builtin_bit_cast(bf16x8, row_ok ? *(const u32x4*)(dp + ds * 16) : u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+    const float lse2 = row_ok ? lse2_of(a.lse[(size_t)head * a.n + row]) : INFINITY;
+    const float dsr = row_ok ? a.dsum[(size_t)head * a.n + row] : 0.0f;
+    const float cs = a.scale * kLog2e;
+    const Frag fr = frag_offsets(lane);
+    const TileLoad lm = tile_load_map(threadIdx.x, (uint32_t)(a.heads * ROWB));
+    f32x16 dq[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
+
+    auto load = [&](int32_t it, char* kt, char* vt) __attribute__((always_inline)) {
+        const int32_t j0 = tiles::tile_at(tr, it) * TR;
+        load_tile((const char*)a.k, j0, a.n, a.heads, head, lm, (char LDS_AS*)kt, wave);
+        load_tile((const char*)a.v, j0, a.n, a.heads, head, lm, (char LDS_AS*)vt, wave);
+    };
+    auto step = [&](int32_t it, const char* kt_, const char* vt_) __attribute__((always_inline)) {
+        const char LDS_AS* kt = (const char LDS_AS*)kt_;
+        const char LDS_AS* vt = (const char LDS_AS*)vt_;
+        const int32_t j0 = tiles::tile_at(tr, it) * TR;
+        const bool full = __builtin_amdgcn_ballot_w64(
+                              !row_ok || ((lo0 <= j0) & (j0 + TR <= hi0)) || ((lo1 <= j0) & (j0 + TR <= hi1))) ==
+                          ~0ull;
+#pragma nounroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < 8; ++ds) {
+                s = mfma(rows_frag(kt, fr, kb, ds), qf[ds], s);
+                dp = mfma(rows_frag(vt, fr, kb, ds), df[ds], dp);
+            }
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                float x[8];
+#pragma unroll
+                for (int r8 = 0; r8 < 8; ++r8) {
+                    const int r = 8 * t + r8;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], cs, -lse2));
+                    if (!full) {
+                        const int32_t j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const uint32_t ok = tiles::in_range(j, lo0, hi0) | tiles::in_range(j, lo1, hi1);
+                        p = ok ? p : 0.0f;
+                    }
+                    x[r8] = p * (dp[r] - dsr);
+                }
+#pragma unroll
+                for (int r8 = 0; r8 < 8; ++r8) dsb[t][r8] = (__bf16)x[r8];
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) dq[db] = mfma(tr_frag(kt, fr, kb, db, t), dsb[t], dq[db]);
+        }
+    };
+
+    if (tr.total > 0) {
+        load(0, k0, v0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    for (int32_t it = 0; it < tr.total; it += 2) {
+        if (it + 1 < tr.total) load(it + 1, k1, v1);
+        if (wave_has_rows) step(it, k0, v0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (it + 1 >= tr.total) break;
+        if (it + 2 < tr.total) load(it + 2, k0, v0);
+        if (wave_has_rows) step(it + 1, k1, v1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    if (row_ok) {
+        __bf16* op = a.dq + (int64_t)row * stride + (int64_t)head * HD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 v4 = {dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale, dq[db][4 * g + 2] * a.scale,
+                            dq[db][4 * g + 3] * a.scale};
+                *(bf16x4*)(op + db * 32 + 8 * g + 4 * h) = __builtin_convertvector(v4, bf16x4);
+            }
+    }
+}
+
+// ---- dK, dV: a workgroup owns BR keys of one head
+__global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) char q0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char q1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char d0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char d1[TILEB];
+    __shared__ __attribute__((aligned(16))) float rowv[2][2][TR];  // [buffer][lse2, D][row of the tile]
+    __shared__ __attribute__((aligned(1024))) char vown[BR * ROWB];  // V of the workgroup's keys (B operand of dP)
+    const int32_t n_tiles = (a.n + BR - 1) / BR;
+    int32_t head, kt;
+    unit_of(blockIdx.x, n_tiles * a.heads, n_tiles, head, kt);
+    const int32_t c0 = kt * BR;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l32 = lane & 31, h = lane >> 5;
+    const int32_t key = c0 + wave * 32 + l32;
+    const bool key_ok = key < a.n;
+    const bool wave_has_keys = c0 + wave * 32 < a.n;
+    const tiles::TileRanges tr = col_tile_ranges(a.mask, a.n, c0, c0 + BR);
+    int32_t lo0, hi0, lo1, hi1;
+    col_ranges(a.mask, a.n, key, lo0, hi0, lo1, hi1);
+
+    const int64_t stride = (int64_t)a.heads * HD;
+    // K^T as B operand in registers: lane = key l32, dims 16 ds + 8 h .. + 7; V^T
+    // (the same fragments of V) is read from LDS, where this workgroup's V rows
+    // stay for the whole loop (registers hold the dK^T, dV^T accumulators)
+    bf16x8 kf[8];
+    {
+        const __bf16* kp = a.k + (int64_t)key * stride + (int64_t)head * HD + h * 8;
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds)
+            kf[ds] = __builtin_bit_cast(bf16x8, key_ok ? *(const u32x4*)(kp + ds * 16) : u32x4{0u, 0u, 0u, 0u});
+    }
+    const float cs = a.scale * kLog2e;
+    const Frag fr = frag_offsets(lane);
+    const TileLoad lm = tile_load_map(threadIdx.x, (uint32_t)(a.heads * ROWB));
+#pragma unroll
+    for (int i = 0; i < BR / TR; ++i)
+        load_tile((const char*)a.v, c0 + i * TR, a.n, a.heads, head, lm, (char LDS_AS*)vown + i * TILEB, wave);
+    const char LDS_AS* vw = (const char LDS_AS*)vown + wave * 32 * ROWB;  // this wave's 32 keys
+    f32x16 dk[4], dv[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    // the tile's row values (lse in log2 units, D) go through registers into LDS
+    float rv_l = 0.0f, rv_d = 0.0f;
+    auto fetch_rows = [&](int32_t it) __attribute__((always_inline)) {
+        const int32_t i = tiles::tile_at(tr, it) * TR + (int32_t)threadIdx.x;
+        if (threadIdx.x < TR) {
+            rv_l = i < a.n ? lse2_of(a.lse[(size_t)head * a.n + i]) : INFINITY;
+            rv_d = i < a.n ? a.dsum[(size_t)head * a.n + i] : 0.0f;
+        }
+    };
+    auto store_rows = [&](int buf) __attribute__((always_inline)) {
+        if (threadIdx.x < TR) {
+            rowv[buf][0][threadIdx.x] = rv_l;
+            rowv[buf][1][threadIdx.x] = rv_d;
+        }
+    };
+    auto load = [&](int32_t it, char* qt, char* dt) __attribute__((always_inline)) {
+        const int32_t i0 = tiles::tile_at(tr, it) * TR;
+        load_tile((const char*)a.q, i0, a.n, a.heads, head, lm, (char LDS_AS*)qt, wave);
+        load_tile((const char*)a.dout, i0, a.n, a.heads, head, lm, (char LDS_AS*)dt, wave);
+    };
+    auto step = [&](int32_t it, const char* qt_, const char* dt_, int buf) __attribute__((always_inline)) {
+        const char LDS_AS* qt = (const char LDS_AS*)qt_;
+        const char LDS_AS* dt = (const char LDS_AS*)dt_;
+        const int32_t i0 = tiles::tile_at(tr, it) * TR;
+        const bool full = __builtin_amdgcn_ballot_w64(
+                              !key_ok || ((lo0 <= i0) & (i0 + TR <= hi0)) || ((lo1 <= i0) & (i0 + TR <= hi1))) ==
+                          ~0ull;
+#pragma nounroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // P first (then its fp32 scores are dead), dV^T += dO^T P; then dP and
+            // dS = P (dP - D) from the bf16 P, dK^T += Q^T dS: fewer live registers
+            f32x16 s = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < 8; ++ds) s = mfma(rows_frag(qt, fr, qb, ds), kf[ds], s);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 pb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    // registers 8t + 4u .. + 3 hold rows 32 qb + 16 t + 8 u + 4 h + {0..3}
+                    const int rr = qb * 32 + 16 * t + 8 * u + 4 * h;
+                    const f32x4 l4 = *(const f32x4*)&rowv[buf][0][rr];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + 4 * u + w], cs, -l4[w]));
+                        if (!full) {
+                            const uint32_t ok = tiles::in_range(i0 + rr + w, lo0, hi0) |
+                                                tiles::in_range(i0 + rr + w, lo1, hi1);
+                            p = ok ? p : 0.0f;
+                        }
+                        pb[t][4 * u + w] = (__bf16)p;
+                    }
+                }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) dv[db] = mfma(tr_frag(dt, fr, qb, db, t), pb[t], dv[db]);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 dp = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < 8; ++ds) dp = mfma(rows_frag(dt, fr, qb, ds), rows_frag(vw, fr, 0, ds), dp);
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int rr = qb * 32 + 16 * t + 8 * u + 4 * h;
+                    const f32x4 d4 = *(const f32x4*)&rowv[buf][1][rr];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        dsb[t][4 * u + w] = (__bf16)((float)pb[t][4 * u + w] * (dp[8 * t + 4 * u + w] - d4[w]));
+                }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) dk[db] = mfma(tr_frag(qt, fr, qb, db, t), dsb[t], dk[db]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (tr.total > 0) {
+        load(0, q0, d0);
+        fetch_rows(0);
+        store_rows(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    for (int32_t it = 0; it < tr.total; it += 2) {
+        if (it + 1 < tr.total) {
+            load(it + 1, q1, d1);
+            fetch_rows(it + 1);
+        }
+        if (wave_has_keys) step(it, q0, d0, 0);
+        if (it + 1 < tr.total) store_rows(1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (it + 1 >= tr.total) break;
+        if (it + 2 < tr.total) {
+            load(it + 2, q0, d0);
+            fetch_rows(it + 2);
+        }
+        if (wave_has_keys) step(it + 1, q1, d1, 1);
+        if (it + 2 < tr.total) store_rows(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    if (key_ok) {
+        __bf16* kp = a.dk + (int64_t)key * stride + (int64_t)head * HD;
+        __bf16* vp = a.dv + (int64_t)key * stride + (int64_t)head * HD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 k4 = {dk[db][4 * g] * a.scale, dk[db][4 * g + 1] * a.scale, dk[db][4 * g + 2] * a.scale,
+                            dk[db][4 * g + 3] * a.scale};
+                f32x4 v4 = {dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+                *(bf16x4*)(kp + db * 32 + 8 * g + 4 * h) = __builtin_convertvector(k4, bf16x4);
+                *(bf16x4*)(vp + db * 32 + 8 * g + 4 * h) = __builtin_convertvector(v4, bf16x4);
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_moba_backward(const MobaBwd& b, hipStream_t s) {
+    if (b.n <= 0 || b.heads <= 0) return hipErrorInvalidValue;
+    BwdArgs a;
+    a.q = (const __bf16*)b.q;
+    a.k = (const __bf16*)b.k;
+    a.v = (const __bf16*)b.v;
+    a.dout = (const __bf16*)b.dout;
+    a.lse = b.lse;
+    a.dsum = b.dsum;
+    a.dq = (__bf16*)b.dq;
+    a.dk = (__bf16*)b.dk;
+    a.dv = (__bf16*)b.dv;
+    a.n = b.n;
+    a.heads = b.heads;
+    a.scale = b.scale;
+    a.mask = b.mask;
+    const int64_t rows = (int64_t)b.n * b.heads;
+    hipLaunchKernelGGL(bwd_dsum_kernel, dim3((uint32_t)((rows * 16 + 255) / 256)), dim3(256), 0, s, (const __bf16*)b.dout,
+                       (const __bf16*)b.out, b.dsum, b.n, b.heads);
+    const uint32_t units = (uint32_t)(((b.n + BR - 1) / BR) * b.heads);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(units), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(units), dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace wmk

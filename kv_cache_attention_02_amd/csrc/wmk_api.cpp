@@ -428,6 +428,42 @@ wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t
     return run_attention(call, hd->dtype, (char*)workspace + need, workspace_bytes - need, stream, &bufs);
 }
 
+// Validate a MoBA call and fill its AttnCall (no workspace, no lse).
+wmk_status moba_call(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k, const void* v,
+                     void* out, float scale, wmk::AttnCall& call) {
+    if (m == nullptr) return fail(WMK_ERR_NULL, "MoBA descriptor is NULL");
+    wmk_status s = check_head(hd);
+    if (s != WMK_OK) return s;
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+        return fail(WMK_ERR_NULL, "q, k, v and out must not be NULL");
+    if (m->tokens_per_frame < 1 || m->frames < 1 || m->chunk_frames < 1)
+        return fail(WMK_ERR_SHAPE, "MoBA descriptor has a non-positive field");
+    if (m->bidir_block != 0 && m->bidir_block != 1) return fail(WMK_ERR_SHAPE, "bidir_block %d not 0 or 1", m->bidir_block);
+    const int64_t L = (int64_t)m->frames * m->tokens_per_frame;
+    const int64_t total = (2 + m->bidir_block) * L;
+    if (total > INT32_MAX) return fail(WMK_ERR_SHAPE, "sequence of %lld tokens exceeds 2^31 - 1", (long long)total);
+    if ((s = check_scale(scale)) != WMK_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(WMK_ERR_ALIGN, "q/k/v/out must be 16-byte aligned");
+    memset(&call, 0, sizeof call);
+    call.kv.k[0] = k;
+    call.kv.v[0] = v;
+    call.kv.end[0] = (int32_t)total;
+    call.kv.n = 1;
+    call.q = q;
+    call.out = out;
+    call.q_tokens = (int32_t)total;
+    call.heads = hd->num_heads;
+    call.head_dim = hd->head_dim;
+    call.kv_total = (int32_t)total;
+    call.scale = scale;
+    call.mask.mode = wmk::kMaskMoba;
+    call.mask.part_len = (int32_t)L;
+    call.mask.chunk_len = std::min(m->chunk_frames, m->frames) * m->tokens_per_frame;
+    call.mask.parts = 2 + m->bidir_block;
+    return WMK_OK;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -590,40 +626,76 @@ wmk_status wmk_chunk_attention_retained(const wmk_cache* c, int32_t layer, const
 wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
                               const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-    if (m == nullptr) return fail(WMK_ERR_NULL, "MoBA descriptor is NULL");
-    wmk_status s = check_head(hd);
-    if (s != WMK_OK) return s;
-    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
-        return fail(WMK_ERR_NULL, "q, k, v and out must not be NULL");
-    if (m->tokens_per_frame < 1 || m->frames < 1 || m->chunk_frames < 1)
-        return fail(WMK_ERR_SHAPE, "MoBA descriptor has a non-positive field");
-    if (m->bidir_block != 0 && m->bidir_block != 1) return fail(WMK_ERR_SHAPE, "bidir_block %d not 0 or 1", m->bidir_block);
-    const int64_t L = (int64_t)m->frames * m->tokens_per_frame;
-    const int64_t total = (2 + m->bidir_block) * L;
-    if (total > INT32_MAX) return fail(WMK_ERR_SHAPE, "sequence of %lld tokens exceeds 2^31 - 1", (long long)total);
-    if ((s = check_scale(scale)) != WMK_OK) return s;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(WMK_ERR_ALIGN, "q/k/v/out must be 16-byte aligned");
     wmk::AttnCall call;
-    memset(&call, 0, sizeof call);
-    call.kv.k[0] = k;
-    call.kv.v[0] = v;
-    call.kv.end[0] = (int32_t)total;
-    call.kv.n = 1;
-    call.q = q;
-    call.out = out;
-    call.q_tokens = (int32_t)total;
-    call.heads = hd->num_heads;
-    call.head_dim = hd->head_dim;
-    call.kv_total = (int32_t)total;
-    call.scale = scale;
-    call.mask.mode = wmk::kMaskMoba;
-    call.mask.part_len = (int32_t)L;
-    call.mask.chunk_len = std::min(m->chunk_frames, m->frames) * m->tokens_per_frame;
-    call.mask.parts = 2 + m->bidir_block;
+    const wmk_status s = moba_call(m, hd, q, k, v, out, scale, call);
+    if (s != WMK_OK) return s;
     (void)workspace;  // MoBA q-tiles differ in cost: longest first, no split tail
     (void)workspace_bytes;
     return run_attention(call, hd->dtype, nullptr, 0, stream);
+}
+
+wmk_status wmk_moba_attention_train(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
+                                    const void* v, void* out, float* lse, float scale, hipStream_t stream) {
+    wmk::AttnCall call;
+    wmk_status s = moba_call(m, hd, q, k, v, out, scale, call);
+    if (s != WMK_OK) return s;
+    if (lse == nullptr) return fail(WMK_ERR_NULL, "lse must not be NULL");
+    if (!aligned16(lse)) return fail(WMK_ERR_ALIGN, "lse must be 16-byte aligned");
+    if (hd->dtype != WMK_BF16) return fail(WMK_ERR_DTYPE, "the training forward takes bf16 inputs");
+    call.lse = lse;
+    return run_attention(call, hd->dtype, nullptr, 0, stream);
+}
+
+size_t wmk_moba_backward_workspace_bytes(const wmk_moba_desc* m, const wmk_head_desc* hd) {
+    if (m == nullptr || check_head(hd) != WMK_OK || m->tokens_per_frame < 1 || m->frames < 1 ||
+        (m->bidir_block != 0 && m->bidir_block != 1))
+        return 0;
+    const int64_t n = (int64_t)(2 + m->bidir_block) * m->frames * m->tokens_per_frame;
+    if (n > INT32_MAX) return 0;
+    return align256((size_t)n * hd->num_heads * sizeof(float));
+}
+
+wmk_status wmk_moba_attention_backward(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
+                                       const void* v, const void* out, const void* dout, const float* lse, void* dq,
+                                       void* dk, void* dv, float scale, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    wmk::AttnCall call;
+    wmk_status s = moba_call(m, hd, q, k, v, const_cast<void*>(out), scale, call);
+    if (s != WMK_OK) return s;
+    if (dout == nullptr || lse == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+        return fail(WMK_ERR_NULL, "dout, lse, dq, dk and dv must not be NULL");
+    if (hd->dtype != WMK_BF16) return fail(WMK_ERR_DTYPE, "the backward takes bf16 inputs");
+    if (hd->head_dim != 128) return fail(WMK_ERR_SHAPE, "the backward is built for head_dim 128");
+    if (!aligned16(dout) || !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return fail(WMK_ERR_ALIGN, "dout/lse/dq/dk/dv must be 16-byte aligned");
+    const size_t need = wmk_moba_backward_workspace_bytes(m, hd);
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(WMK_ERR_CAPACITY, "the backward needs %zu bytes of workspace, got %zu", need, workspace_bytes);
+    if (!aligned16(workspace)) return fail(WMK_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
+    if (dry_run_path() != nullptr) {
+        dry_log("moba_bwd n=%d heads=%d part=%d chunk=%d parts=%d\n", call.q_tokens, call.heads, call.mask.part_len,
+                call.mask.chunk_len, call.mask.parts);
+        return ok();
+    }
+    wmk::MobaBwd b;
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.out = out;
+    b.dout = dout;
+    b.lse = lse;
+    b.dsum = (float*)workspace;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.n = call.q_tokens;
+    b.heads = call.heads;
+    b.scale = scale;
+    b.mask = call.mask;
+    const hipError_t e = wmk::launch_moba_backward(b, stream);
+    if (e != hipSuccess) return fail(WMK_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 wmk_status wmk_cross_attention_train(const wmk_xattn_desc* x, const wmk_head_desc* hd, const void* q, const void* k,

@@ -58,6 +58,7 @@ struct AttnCallN {
     float scale;
     KvSpansN<N> kv;
     MaskShape mask;
+    float* lse;  // optional [heads][q_tokens] natural-log sum of exp of the scaled scores (NULL: not written)
 };
 using AttnCall = AttnCallN<kMaxSeg>;
 
@@ -103,6 +104,27 @@ size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t split
 // kernel's LDS layout; rows = 32: plain row-major query blocks).  head_dim 128.
 hipError_t launch_quant_e4m3(const void* const* src, const int32_t* end, int n_spans, int32_t tokens, int32_t heads,
                              int head_dim, int rows, uint8_t* codes, float* scales, hipStream_t s);
+
+// Backward of the MoBA-masked attention (bf16, head_dim 128): all tensors
+// [n][heads][128] bf16 except lse ([heads][n] natural log, from the forward)
+// and dsum ([heads][n] fp32 scratch for D = dO . O).
+struct MobaBwd {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    float* dsum;
+    void* dq;
+    void* dk;
+    void* dv;
+    int32_t n;
+    int32_t heads;
+    float scale;
+    MaskShape mask;
+};
+hipError_t launch_moba_backward(const MobaBwd& b, hipStream_t s);
 
 // fp32 attention (plain SIMT; correctness path for fp32 inputs).
 hipError_t launch_attn_f32(const AttnCall& c, hipStream_t s);
