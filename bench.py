@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--skip-extra", action="store_true", help="skip the other workloads (same as --extra none)")
     ap.add_argument("--extra", default="all",
-                    help="other workloads to run, comma separated: moba, 720p, qk8, retained, rolling, cross_train "
+                    help="other workloads to run, comma separated: moba, moba_bwd, 720p, qk8, retained, rolling, "
+                         "cross_train "
                          "(or all, none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -204,7 +205,7 @@ def main():
         result["copy_calibration_bytes"] = 2 * n
 
     extra = set() if args.skip_extra or args.extra == "none" else (
-        {"moba", "720p", "qk8", "retained", "rolling", "cross_train"} if args.extra == "all" else set(args.extra.split(",")))
+        {"moba", "moba_bwd", "720p", "qk8", "retained", "rolling", "cross_train"} if args.extra == "all" else set(args.extra.split(",")))
     if extra:
         result["other_workloads"] = other_workloads(wmk, synth, torch, np, fill, dev, stream, reps=5, which=extra)
 
@@ -245,6 +246,28 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps, which):
                              "frac_peak": round(mflops / avg / 1e9 / PEAK_BF16_TFLOPS, 4),
                              "allowed_pairs_per_head": pairs, "dense_fraction": round(945 / 3969, 4)}
         del mq, mk, mv, mo
+
+    if "moba_bwd" in which:
+        # MoBA training step on the same sequence: forward with log-sum-exp, then the
+        # backward (dq, dk, dv); FLOPs of the backward counted as 2.5x the forward's
+        # (five products per allowed pair instead of two)
+        tpf, frames, cf = 1560, 21, 3
+        n = 3 * frames * tpf
+        bq, bk, bv, bdo = (fill((n, H, D), kind=t) for t in (synth.Q, synth.K, synth.V, synth.KLOC))
+        bo, blse = wmk.moba_attention_train(bq, bk, bv, tokens_per_frame=tpf, frames=frames, chunk_frames=cf)
+        fwd_flops = 4.0 * D * H * 945 * tpf * tpf
+        avg_f, mn_f = timed(lambda: wmk.moba_attention_train(bq, bk, bv, tokens_per_frame=tpf, frames=frames,
+                                                             chunk_frames=cf, out=bo, lse=blse))
+        avg_b, mn_b = timed(lambda: wmk.moba_attention_backward(bq, bk, bv, bo, bdo, blse, tokens_per_frame=tpf,
+                                                                frames=frames, chunk_frames=cf))
+        res["moba_98280_train"] = {
+            "fwd_ms_avg": round(avg_f, 3), "bwd_ms_avg": round(avg_b, 3), "bwd_ms_min": round(mn_b, 3),
+            "fwd_tflops": round(fwd_flops / avg_f / 1e9, 1),
+            "bwd_tflops": round(2.5 * fwd_flops / avg_b / 1e9, 1),
+            "bwd_frac_peak": round(2.5 * fwd_flops / avg_b / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "bwd_flops": 2.5 * fwd_flops}
+        del bq, bk, bv, bdo, bo, blse
+        torch.cuda.empty_cache()
 
     if "720p" in which:
         # 720p step: 3600 tokens per frame, 24 heads, 18 slots; chunk-causal cross-attention
