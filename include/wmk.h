@@ -146,9 +146,10 @@ wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new
 wmk_status wmk_cache_slots(const wmk_cache* c, int32_t layer, int64_t* frame_of_slot, int64_t* frames_appended);
 
 /* Bytes of optional scratch that lets the attention calls below split the last,
- * partly filled round of work units over the whole GPU (a split-KV tail with an
- * in-kernel merge).  Passing less (or NULL) is valid and only disables that
- * split.  q_tokens and heads are those of the call. */
+ * partly filled round of work units over the whole GPU (a split-KV tail: the
+ * pieces write fp32 partial results, a second small kernel on the same stream
+ * merges them).  Passing less, NULL, or a pointer not 16-byte aligned is valid
+ * and only disables that split.  q_tokens and heads are those of the call. */
 size_t wmk_attention_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens);
 
 /* Chunk attention at a denoising step: every query row of the current chunk

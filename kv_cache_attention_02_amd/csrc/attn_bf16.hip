@@ -406,15 +406,19 @@ __device__ __forceinline__ float load_f32_vmem(const float* ptr, bool ok) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(ptr, ok ? 4u : 0u), 0, 0, 0));
 }
 
-// Workspace of the split tail: per split unit a counter, then per piece the
-// unnormalized O (BQ x D fp32) and per-row (max reference, sum).
+// Workspace of the split tail: per piece the unnormalized O (BQ x D fp32) and
+// per row (max reference, sum); merged by attn_merge_kernel after the
+// attention kernel (stream order makes the pieces visible: no fences, no
+// counters -- device-scope fences between pieces on different XCDs cost more
+// than the whole tail).
 template <int D>
 struct SplitWs {
     static constexpr size_t kO = (size_t)BQ * D;
-    static __device__ __forceinline__ int* counters(void* ws) { return (int*)ws; }
-    static __device__ __forceinline__ float* piece(void* ws, int32_t n_units, int32_t idx) {
-        const size_t head = ((size_t)n_units * sizeof(int) + 255) & ~(size_t)255;
-        return (float*)((char*)ws + head) + (size_t)idx * (kO + 2 * BQ);
+    static __device__ __forceinline__ float* piece(void* ws, int32_t idx) {
+        return (float*)ws + (size_t)idx * (kO + 2 * BQ);
+    }
+    static __device__ __forceinline__ const float* piece(const void* ws, int32_t idx) {
+        return (const float*)ws + (size_t)idx * (kO + 2 * BQ);
     }
 };
 
@@ -447,7 +451,6 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     };
     const Buf<D> kb0 = mkbuf(k0p0, k0p1), kb1 = mkbuf(k1p0, k1p1);
     const Buf<D> vb0 = mkbuf(v0p0, v0p1), vb1 = mkbuf(v1p0, v1p1);
-    __shared__ int s_last;
 
     // ---- which unit (head, q-tile) and which key-tile range this workgroup runs
     const int32_t b = blockIdx.x;
@@ -918,77 +921,67 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         return;
     }
 
-    // ---- split tail: publish this piece, the last piece of the unit merges
+    // ---- split tail: publish this piece; attn_merge_kernel combines the pieces
     const int32_t su = u - full_units;
-    {
-        float* w = SplitWs<D>::piece(p.ws, p.split_units, su * p.splits + piece);
-        const int rl = wave * 32 + l32;  // row within the tile
+    float* w = SplitWs<D>::piece(p.ws, su * p.splits + piece);
+    const int rl = wave * 32 + l32;  // row within the tile
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *(f32x4*)(w + (size_t)rl * D + db * 32 + 8 * g + 4 * h) =
-                    f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-        if (h == 0) {
-            w[SplitWs<D>::kO + 2 * rl] = m_ref;
-            w[SplitWs<D>::kO + 2 * rl + 1] = l_tot;
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int prev = atomicAdd(SplitWs<D>::counters(p.ws) + su, 1);
-        s_last = (prev == p.splits - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // merge: thread t handles row t/2, half (t%2) of the dims
-    {
-        const int rl = threadIdx.x >> 1, half = threadIdx.x & 1;
-        const int32_t mrow = r0 + rl;
-        float mmax = -INFINITY;
-        for (int q = 0; q < p.splits; ++q) {
-            const float* w = SplitWs<D>::piece(p.ws, p.split_units, su * p.splits + q);
-            mmax = fmaxf(mmax, __builtin_nontemporal_load(w + SplitWs<D>::kO + 2 * rl));
-        }
-        const float mref = (mmax == -INFINITY) ? 0.0f : mmax;
-        float acc[D / 2];
-#pragma unroll
-        for (int d = 0; d < D / 2; ++d) acc[d] = 0.0f;
-        float lt = 0.0f;
-        for (int q = 0; q < p.splits; ++q) {
-            const float* w = SplitWs<D>::piece(p.ws, p.split_units, su * p.splits + q);
-            const float wq = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(w + SplitWs<D>::kO + 2 * rl) - mref);
-            lt += wq * __builtin_nontemporal_load(w + SplitWs<D>::kO + 2 * rl + 1);
-            const float* src = w + (size_t)rl * D + half * (D / 2);
-#pragma unroll
-            for (int d = 0; d < D / 2; d += 4) {
-                const f32x4 x = __builtin_nontemporal_load((const f32x4*)(src + d));
-                acc[d] += wq * x[0];
-                acc[d + 1] += wq * x[1];
-                acc[d + 2] += wq * x[2];
-                acc[d + 3] += wq * x[3];
-            }
-        }
-        if (mrow < c.q_tokens) {
-            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-            if (c.lse != nullptr && half == 0)
-                c.lse[(size_t)head * c.q_tokens + mrow] = lt > 0.0f ? (mref + log2f(lt)) * kLn2 : -INFINITY;
-            __bf16* dst = (__bf16*)c.out + (int64_t)mrow * stride + (int64_t)head * D + half * (D / 2);
-#pragma unroll
-            for (int d = 0; d < D / 2; d += 4) {
-                f32x4 v4 = {acc[d] * inv, acc[d + 1] * inv, acc[d + 2] * inv, acc[d + 3] * inv};
-                *(bf16x4*)(dst + d) = __builtin_convertvector(v4, bf16x4);
-            }
-        }
-        if (threadIdx.x == 0) SplitWs<D>::counters(p.ws)[su] = 0;  // leave the counter zeroed
+        for (int g = 0; g < 4; ++g)
+            *(f32x4*)(w + (size_t)rl * D + db * 32 + 8 * g + 4 * h) =
+                f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+    if (h == 0) {
+        w[SplitWs<D>::kO + 2 * rl] = m_ref;
+        w[SplitWs<D>::kO + 2 * rl + 1] = l_tot;
     }
 }
 
-__global__ void zero_ints(int* p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
+// Merge of the split tail: out = sum_q 2^(m_q - M) O_q / sum_q 2^(m_q - M) l_q
+// with M = max_q m_q, per row; one thread per (split unit, row, 8 dims).
+struct MergeArgs {
+    const void* ws;
+    __bf16* out;
+    float* lse;
+    int32_t q_tokens;
+    int32_t heads;
+    int32_t n_qtiles;
+    int32_t full_units;
+    int32_t split_units;
+    int32_t splits;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+    constexpr int TPR = D / 8;  // threads per row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)a.split_units * BQ * TPR) return;
+    const int32_t su = (int32_t)(gid / (BQ * TPR)), rem = (int32_t)(gid % (BQ * TPR));
+    const int32_t rl = rem / TPR, part = rem % TPR;
+    const int32_t u = a.full_units + su;
+    const int32_t head = u / a.n_qtiles, qt = u % a.n_qtiles;  // units in head-major order (no MoBA groups)
+    const int32_t row = qt * BQ + rl;
+    if (row >= a.q_tokens) return;
+    float mmax = -INFINITY;
+    for (int q = 0; q < a.splits; ++q)
+        mmax = fmaxf(mmax, SplitWs<D>::piece(a.ws, su * a.splits + q)[SplitWs<D>::kO + 2 * rl]);
+    const float mref = (mmax == -INFINITY) ? 0.0f : mmax;
+    f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lt = 0.0f;
+    for (int q = 0; q < a.splits; ++q) {
+        const float* w = SplitWs<D>::piece(a.ws, su * a.splits + q);
+        const float wq = __builtin_amdgcn_exp2f(w[SplitWs<D>::kO + 2 * rl] - mref);
+        lt += wq * w[SplitWs<D>::kO + 2 * rl + 1];
+        const f32x4* src = (const f32x4*)(w + (size_t)rl * D + part * 8);
+        acc0 += wq * src[0];
+        acc1 += wq * src[1];
+    }
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (a.lse != nullptr && part == 0)
+        a.lse[(size_t)head * a.q_tokens + row] = lt > 0.0f ? (mref + log2f(lt)) * kLn2 : -INFINITY;
+    __bf16* dst = a.out + ((int64_t)row * a.heads + head) * D + part * 8;
+    *(bf16x4*)dst = __builtin_convertvector(acc0 * inv, bf16x4);
+    *(bf16x4*)(dst + 4) = __builtin_convertvector(acc1 * inv, bf16x4);
 }
 
 }  // namespace
@@ -997,8 +990,7 @@ int attn_bf16_block_q() { return BQ; }
 
 size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t splits) {
     if (split_units <= 0 || splits <= 0) return 0;
-    const size_t head = ((size_t)split_units * sizeof(int) + 255) & ~(size_t)255;
-    return head + (size_t)split_units * splits * ((size_t)BQ * head_dim + 2 * BQ) * sizeof(float);
+    return (size_t)split_units * splits * ((size_t)BQ * head_dim + 2 * BQ) * sizeof(float);
 }
 
 int attn_bf16_blocks_per_cu(int head_dim) {
@@ -1047,13 +1039,28 @@ hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t
     if (plan.k8 != nullptr && (c.head_dim != 128 || plan.q8 == nullptr || plan.k8_scale == nullptr ||
                                plan.q8_scale == nullptr))
         return hipErrorInvalidValue;
-    if (plan.split_units > 0) {
-        hipLaunchKernelGGL(zero_ints, dim3((plan.split_units + 255) / 256), dim3(256), 0, s, (int*)plan.ws,
-                           plan.split_units);
-    }
     // one cache run plus up to 4 segments (every call but a retained subset of
     // scattered frames): a span table small enough to stay in scalar registers
-    return c.kv.n <= kFewSeg ? launch_spans<kFewSeg>(c, plan, blocks, s) : launch_spans<kMaxSeg>(c, plan, blocks, s);
+    const hipError_t e =
+        c.kv.n <= kFewSeg ? launch_spans<kFewSeg>(c, plan, blocks, s) : launch_spans<kMaxSeg>(c, plan, blocks, s);
+    if (e != hipSuccess || plan.split_units <= 0) return e;
+    MergeArgs m;
+    m.ws = plan.ws;
+    m.out = (__bf16*)c.out;
+    m.lse = plan.k8 != nullptr ? nullptr : c.lse;
+    m.q_tokens = c.q_tokens;
+    m.heads = c.heads;
+    m.n_qtiles = plan.n_qtiles;
+    m.full_units = plan.n_units - plan.split_units;
+    m.split_units = plan.split_units;
+    m.splits = plan.splits;
+    const int64_t threads = (int64_t)plan.split_units * BQ * (c.head_dim / 8);
+    const dim3 grid((uint32_t)((threads + 255) / 256));
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(256), 0, s, m);
+    else
+        hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(256), 0, s, m);
+    return hipGetLastError();
 }
 
 }  // namespace wmk

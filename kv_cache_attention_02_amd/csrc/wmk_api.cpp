@@ -162,7 +162,8 @@ void plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws
     p.split_units = 0;
     p.splits = 1;
     p.ws = nullptr;
-    if (ws == nullptr || tiles_per_unit < 2 * kMinTilesPerPiece) return;
+    // (the pieces store 16-byte vectors: a misaligned workspace is not used)
+    if (ws == nullptr || ((uintptr_t)ws & 15) != 0 || tiles_per_unit < 2 * kMinTilesPerPiece) return;
     const DeviceInfo di = device_info();
     const int slots = di.cus * (head_dim == 64 ? di.bpc64 : di.bpc128);
     if (slots <= 0) return;
