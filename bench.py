@@ -177,7 +177,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(flops / (attn_avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": pmc_traffic(),
-            "kernel": "attn_bf16_kernel<128>",
+            "kernel": "attn_bf16_kernel<128> + attn_merge_kernel<128> (one call: the split tail's merge runs "
+                      "as a second short kernel; both are in the event bracket)",
             "launch_ms_avg": round(attn_avg, 4),
             "launch_ms_median": round(float(np.median(attn_ms)), 4),
             "launch_ms_min": round(float(attn_ms.min()), 4),
