@@ -45,6 +45,10 @@ def parse():
                          "cross_train "
                          "(or all, none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--occupancy-scan", action="store_true",
+                    help="also time the attention kernel at 32, 256 and 2048 workgroups (12 heads' shape, "
+                         "27136 keys): per-step time against occupancy (pair with a GRBM_GUI_ACTIVE counter pass "
+                         "to read the shader clock)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -205,6 +209,9 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 2 * n
 
+    if args.occupancy_scan:
+        result["occupancy_scan"] = occupancy_scan(wmk, synth, torch, fill)
+
     extra = set() if args.skip_extra or args.extra == "none" else (
         {"moba", "moba_bwd", "720p", "qk8", "retained", "rolling", "cross_train"} if args.extra == "all" else set(args.extra.split(",")))
     if extra:
@@ -215,6 +222,33 @@ def main():
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(args, flops, nq, kv_tokens)
     print(json.dumps(result))
+
+
+def occupancy_scan(wmk, synth, torch, fill):
+    """Chunk attention over 27136 keys (424 tiles, no cache, no split tail) at grid sizes
+    32 (one head, 32 q-tiles: 32 CUs busy), 256 (8 heads x 32 q-tiles: every CU once) and
+    2048 (8 rounds): time per 64-key step of a workgroup."""
+    nkv, res = 27136, {}
+    for heads, nq in ((1, 8192), (8, 8192), (8, 65536)):
+        q = fill((nq, heads, D), kind=synth.Q)
+        k, v = fill((nkv, heads, D), kind=synth.K), fill((nkv, heads, D), kind=synth.V)
+        o = torch.empty_like(q)
+        for _ in range(2):
+            wmk.chunk_attention(None, 0, q, [(k, v)], out=o, use_workspace=False)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            wmk.chunk_attention(None, 0, q, [(k, v)], out=o, use_workspace=False)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        wgs = heads * nq // 256
+        rounds = -(-wgs // 256)
+        res[f"{wgs}_workgroups"] = {"ms": round(ms, 4), "us_per_step": round(ms * 1e3 / (rounds * nkv // 64), 3),
+                                    "tflops": round(4.0 * D * heads * nq * nkv / ms / 1e9, 1)}
+        del q, k, v, o
+    return res
 
 
 def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps, which):
