@@ -501,3 +501,42 @@ def test_qk8_workspace_errors_and_plan(lib, dry):
     assert q["qk8"] == "0" and (p["split_units"], p["splits"]) == (q["split_units"], q["splits"])
     assert int(p["split_units"]) > 0
     lib.wmk_cache_destroy(h)
+
+
+def test_moba_train_and_backward_argument_errors(lib, dry):
+    """Training forward (with log-sum-exp) and backward: argument checks before anything is
+    planned; a valid backward logs its plan."""
+    md = wmk.wmk_moba_desc(1560, 21, 3, 1)
+    hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
+    LSE, DO, DQ, DK, DV, WS = 0x61000000, 0x62000000, 0x63000000, 0x64000000, 0x65000000, 0x66000000
+    n = 3 * 21 * 1560
+    need = lib.wmk_moba_backward_workspace_bytes(ctypes.byref(md), ctypes.byref(hd))
+    assert need == (n * 12 * 4 + 255) // 256 * 256
+    assert lib.wmk_moba_backward_workspace_bytes(None, ctypes.byref(hd)) == 0
+    fwd = lambda **kw: lib.wmk_moba_attention_train(
+        ctypes.byref(kw.get("md", md)), ctypes.byref(kw.get("hd", hd)), QBUF, KBUF, VBUF, OBUF, kw.get("lse", LSE),
+        kw.get("scale", 0.088), None)
+    bwd = lambda **kw: lib.wmk_moba_attention_backward(
+        ctypes.byref(kw.get("md", md)), ctypes.byref(kw.get("hd", hd)), QBUF, KBUF, VBUF, OBUF, kw.get("dout", DO),
+        kw.get("lse", LSE), kw.get("dq", DQ), DK, DV, kw.get("scale", 0.088), kw.get("ws", WS),
+        kw.get("wsb", need), None)
+    bad = [
+        (fwd, dict(lse=0), wmk.WMK_ERR_NULL), (fwd, dict(lse=LSE + 4), wmk.WMK_ERR_ALIGN),
+        (fwd, dict(hd=wmk.wmk_head_desc(12, 128, wmk.WMK_F32)), wmk.WMK_ERR_DTYPE),
+        (fwd, dict(scale=-1.0), wmk.WMK_ERR_RANGE),
+        (bwd, dict(dout=0), wmk.WMK_ERR_NULL), (bwd, dict(dq=0), wmk.WMK_ERR_NULL),
+        (bwd, dict(dq=DQ + 2), wmk.WMK_ERR_ALIGN),
+        (bwd, dict(hd=wmk.wmk_head_desc(12, 64, wmk.WMK_BF16)), wmk.WMK_ERR_SHAPE),
+        (bwd, dict(hd=wmk.wmk_head_desc(12, 128, wmk.WMK_F32)), wmk.WMK_ERR_DTYPE),
+        (bwd, dict(ws=0), wmk.WMK_ERR_CAPACITY), (bwd, dict(wsb=need - 4), wmk.WMK_ERR_CAPACITY),
+        (bwd, dict(md=wmk.wmk_moba_desc(1560, 21, 3, 2)), wmk.WMK_ERR_SHAPE),
+    ]
+    for fn, kw, status in bad:
+        n_before = len(dry.read_text().splitlines()) if dry.exists() else 0
+        assert fn(**kw) == status, (kw, status)
+        assert (len(dry.read_text().splitlines()) if dry.exists() else 0) == n_before
+    assert fwd() == wmk.WMK_OK
+    assert _last_attn(dry)["mask"] == "1"
+    assert bwd() == wmk.WMK_OK
+    last = dry.read_text().strip().splitlines()[-1]
+    assert last == f"moba_bwd n={n} heads=12 part={21 * 1560} chunk={3 * 1560} parts=3"
