@@ -2,8 +2,9 @@
 //
 // One workgroup = 8 waves = 256 query rows of one head (32 rows per wave); keys
 // are visited in tiles of 64.  K and V tiles go from global memory straight
-// into LDS (global_load_lds_dwordx4, no staging registers) and are shared by
-// the 8 waves; two K and two V buffers, one barrier per tile.
+// into LDS (16-byte buffer loads with the LDS-destination form, no staging
+// registers) and are shared by the 8 waves; two K and two V buffers, one
+// barrier per tile.
 //
 // Per wave, iteration j (software pipelined across tiles):
 //   softmax of tile j            fp32, log2 domain: exp2 with scale*log2(e)
@@ -33,6 +34,12 @@
 // visited tile applies the per-element interval test.  Tiles that no row of
 // the workgroup allows are never visited: the workgroup walks only the union of
 // its rows' ranges, in tile units.
+//
+// Split tail: when there are too few units (256-row query tiles of one head)
+// to fill the chip, the last units are cut into pieces along their key tiles.
+// Each piece writes its unnormalized O and per-row (max, sum) to a workspace;
+// attn_merge_kernel, launched after it on the same stream, combines the pieces
+// of a unit.  No piece waits on another.
 //
 // FP8 variant (Q8): Q and K arrive pre-quantized to e4m3 with one fp32 scale per
 // block (32 query rows of a wave; one 64-key tile), the K tile already in the
