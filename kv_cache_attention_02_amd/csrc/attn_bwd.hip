@@ -88,6 +88,22 @@ __device__ __forceinline__ bf16x8 rows_frag(const char LDS_AS* tile, const Frag&
     return *(const bf16x8 LDS_AS*)(tile + kb * 32 * ROWB + f.base + (f.xr ^ (uint32_t)(32 * ds)));
 }
 
+// The eight row-read offsets base + (xr ^ 32 ds) as separate values: every
+// read is then one of them plus a compile-time offset (the tile object and the
+// row block fold into the instruction's immediate).
+struct RowOff {
+    uint32_t o[8];
+};
+__device__ __forceinline__ RowOff row_offsets(const Frag& f) {
+    RowOff r;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) r.o[ds] = f.base + (f.xr ^ (uint32_t)(32 * ds));
+    return r;
+}
+__device__ __forceinline__ bf16x8 rows_frag(const char LDS_AS* tile, const RowOff& ro, int kb, int ds) {
+    return *(const bf16x8 LDS_AS*)(tile + kb * 32 * ROWB + ro.o[ds]);
+}
+
 // A operand transposed: dim 32 db + lane%32, the 8 rows 32 kb + 16 t + 8 u + 4 h + {0..3}
 // (u = 0, 1) -- the row order of registers 8t .. 8t+7 of a 32x32 accumulator
 __device__ __forceinline__ bf16x8 tr_frag(const char LDS_AS* tile, const Frag& f, int kb, int db, int t) {
@@ -98,12 +114,27 @@ __device__ __forceinline__ bf16x8 tr_frag(const char LDS_AS* tile, const Frag& f
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Keeps a value computed where it is written: an empty asm statement that
+// reads and rewrites it, so the optimizer cannot sink its computation past this
+// point (next to its use, after the MFMAs it is meant to run beside).
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// A buffer resource from values the caller knows to be uniform, moved to scalar
+// registers explicitly (a clamp done on the VALU would otherwise leave them in
+// vector registers, and every load through the resource in a per-lane loop).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_uniform(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes));
 }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, char LDS_AS* dst) {
@@ -229,6 +260,52 @@ __device__ __forceinline__ void unit_of(int32_t b, int32_t units, int32_t n_tile
     t = u % n_tiles;
 }
 
+// The tile ranges depend only on the workgroup; say so to the compiler, so
+// that the buffer resources built from them stay in scalar registers (the
+// direct loads then need no per-lane loop).
+__device__ __forceinline__ tiles::TileRanges uniform(tiles::TileRanges r) {
+    r.b0 = __builtin_amdgcn_readfirstlane(r.b0);
+    r.e0 = __builtin_amdgcn_readfirstlane(r.e0);
+    r.b1 = __builtin_amdgcn_readfirstlane(r.b1);
+    r.e1 = __builtin_amdgcn_readfirstlane(r.e1);
+    r.b2 = __builtin_amdgcn_readfirstlane(r.b2);
+    r.e2 = __builtin_amdgcn_readfirstlane(r.e2);
+    r.b3 = __builtin_amdgcn_readfirstlane(r.b3);
+    r.e3 = __builtin_amdgcn_readfirstlane(r.e3);
+    r.total = __builtin_amdgcn_readfirstlane(r.total);
+    return r;
+}
+
+// The next tile's direct loads, issued in four pieces per thread (rows 0-31
+// and 32-63 of the first tensor, then of the second) spread over the first
+// MFMA group of a step: a wave that issues them all at once stalls on the
+// load interface.
+struct NextTile {
+    __amdgpu_buffer_rsrc_t r0, r1;
+    char LDS_AS* t0;
+    char LDS_AS* t1;
+    bool ok;
+};
+__device__ __forceinline__ NextTile next_tile(const tiles::TileRanges& tr, int32_t it, const __bf16* src0,
+                                              const __bf16* src1, int32_t n, int32_t heads, int32_t head, char* t0,
+                                              char* t1) {
+    NextTile x;
+    x.ok = it < tr.total;
+    const int32_t r0 = x.ok ? tiles::tile_at(tr, it) * TR : 0;
+    const uint32_t bytes = x.ok ? (uint32_t)max(0, min(TR, n - r0)) * (uint32_t)heads * ROWB : 0u;
+    const size_t off = ((size_t)r0 * heads + head) * ROWB;
+    x.r0 = rsrc_uniform((const char*)src0 + off, bytes);
+    x.r1 = rsrc_uniform((const char*)src1 + off, bytes);
+    x.t0 = (char LDS_AS*)t0;
+    x.t1 = (char LDS_AS*)t1;
+    return x;
+}
+__device__ __forceinline__ void next_piece(const NextTile& x, const TileLoad& m, int wave, int i) {
+    if (!x.ok) return;
+    if (i < 2) dma16(x.r0, m.off[i], x.t0 + i * (TILEB / 2) + wave * 1024);
+    else dma16(x.r1, m.off[i - 2], x.t1 + (i - 2) * (TILEB / 2) + wave * 1024);
+}
+
 // ---- dQ: a workgroup owns BR query rows of one head
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char k0[TILEB];
@@ -250,7 +327,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     rc.q_tokens = a.n;
     rc.kv_total = a.n;
     rc.mask = a.mask;
-    const tiles::TileRanges tr = tiles::tile_ranges(rc, r0, r1);
+    const tiles::TileRanges tr = uniform(tiles::tile_ranges(rc, r0, r1));
     int32_t lo0, hi0, lo1, hi1;
     tiles::row_ranges(rc, row, lo0, hi0, lo1, hi1);
 
@@ -269,71 +346,133 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     const float dsr = row_ok ? a.dsum[(size_t)head * a.n + row] : 0.0f;
     const float cs = a.scale * kLog2e;
     const Frag fr = frag_offsets(lane);
+    const RowOff ro = row_offsets(fr);
     const TileLoad lm = tile_load_map(threadIdx.x, (uint32_t)(a.heads * ROWB));
     f32x16 dq[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) dq[db] = f32x16{};
 
-    auto load = [&](int32_t it, char* kt, char* vt) __attribute__((always_inline)) {
-        const int32_t j0 = tiles::tile_at(tr, it) * TR;
-        load_tile((const char*)a.k, j0, a.n, a.heads, head, lm, (char LDS_AS*)kt, wave);
-        load_tile((const char*)a.v, j0, a.n, a.heads, head, lm, (char LDS_AS*)vt, wave);
-    };
-    auto step = [&](int32_t it, const char* kt_, const char* vt_) __attribute__((always_inline)) {
+    // One key tile, two halves of 32 keys, in this written order (a scheduling
+    // fence after each MFMA group keeps it):
+    //   A0   S^T, dP^T of half 0 (16 MFMAs; the next tile's loads spread here)
+    //   V0   dS^T of half 0 (VALU)
+    //   A1   S^T, dP^T of half 1
+    //   B0   dQ^T += K^T dS^T of half 0 (8 MFMAs), beside dS^T of half 1
+    //   B1   dQ^T += K^T dS^T of half 1
+    // Row fragments are read two k-steps ahead, K^T fragments two MFMAs ahead,
+    // and the first reads of a group are made in the last steps of the one before.
+    // full: every row of the wave allows the whole tile (the mask code is skipped)
+    auto step = [&](bool full, int32_t j0, const char* kt_, const char* vt_, const NextTile& nx)
+                    __attribute__((always_inline)) {
         const char LDS_AS* kt = (const char LDS_AS*)kt_;
         const char LDS_AS* vt = (const char LDS_AS*)vt_;
-        const int32_t j0 = tiles::tile_at(tr, it) * TR;
-        const bool full = __builtin_amdgcn_ballot_w64(
-                              !row_ok || ((lo0 <= j0) & (j0 + TR <= hi0)) || ((lo1 <= j0) & (j0 + TR <= hi1))) ==
-                          ~0ull;
-#pragma nounroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+        bf16x8 kr[2][8], vr[2][8], kq[2][8];  // fragments, each read once (registers follow liveness)
+        auto rows = [&](int kb, int ds) __attribute__((always_inline)) {
+            kr[kb][ds] = rows_frag(kt, ro, kb, ds);
+            vr[kb][ds] = rows_frag(vt, ro, kb, ds);
+        };
+        auto trs = [&](int kb, int m) __attribute__((always_inline)) { kq[kb][m] = tr_frag(kt, fr, kb, m >> 1, m & 1); };
+        f32x16 s, dp;
+        // masked keys get a score of -inf (weight 0); one uniform branch per half
+        auto mask = [&](int kb) __attribute__((always_inline)) {
+            if (full) return;
 #pragma unroll
-            for (int ds = 0; ds < 8; ++ds) {
-                s = mfma(rows_frag(kt, fr, kb, ds), qf[ds], s);
-                dp = mfma(rows_frag(vt, fr, kb, ds), df[ds], dp);
+            for (int r = 0; r < 16; ++r) {
+                const int32_t j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const uint32_t ok = tiles::in_range(j, lo0, hi0) | tiles::in_range(j, lo1, hi1);
+                s[r] = ok ? s[r] : -INFINITY;
             }
-            bf16x8 dsb[2];
+        };
+        // dS^T = P^T (dP^T - D) for accumulator registers 4g .. 4g + 3, in bf16
+        auto dsg = [&](int g, bf16x8* dsb) __attribute__((always_inline)) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                float x[8];
-#pragma unroll
-                for (int r8 = 0; r8 < 8; ++r8) {
-                    const int r = 8 * t + r8;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], cs, -lse2));
-                    if (!full) {
-                        const int32_t j = j0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const uint32_t ok = tiles::in_range(j, lo0, hi0) | tiles::in_range(j, lo1, hi1);
-                        p = ok ? p : 0.0f;
-                    }
-                    x[r8] = p * (dp[r] - dsr);
-                }
-#pragma unroll
-                for (int r8 = 0; r8 < 8; ++r8) dsb[t][r8] = (__bf16)x[r8];
+            for (int w = 0; w < 4; ++w) {
+                const int r = 4 * g + w;
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], cs, -lse2));
+                dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dsr));
             }
+        };
+        bf16x8 ds0[2], ds1[2];
+        // A0
+        rows(0, 0);
+        rows(0, 1);
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) dq[db] = mfma(tr_frag(kt, fr, kb, db, t), dsb[t], dq[db]);
+        for (int ds = 0; ds < 8; ++ds) {
+            if (ds + 2 < 8) rows(0, ds + 2);
+            else rows(1, ds - 6);
+            s = mfma(kr[0][ds], qf[ds], s);
+            dp = mfma(vr[0][ds], df[ds], dp);
+            if (ds & 1) next_piece(nx, lm, wave, ds >> 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // V0
+        mask(0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dsg(g, ds0);
+        pin(ds0[0]);
+        pin(ds0[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        // A1
+        s = f32x16{};
+        dp = f32x16{};
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+            if (ds + 2 < 8) rows(1, ds + 2);
+            else trs(0, ds - 6);
+            s = mfma(kr[1][ds], qf[ds], s);
+            dp = mfma(vr[1][ds], df[ds], dp);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mask(1);
+        __builtin_amdgcn_sched_barrier(0);
+        // B0 beside V1
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            if (m + 2 < 8) trs(0, m + 2);
+            else trs(1, m - 6);
+            dq[m >> 1] = mfma(kq[0][m], ds0[m & 1], dq[m >> 1]);
+            if (m & 1) {
+                dsg(m >> 1, ds1);
+                pin(ds1[m >> 2]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // B1
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            if (m + 2 < 8) trs(1, m + 2);
+            dq[m >> 1] = mfma(kq[1][m], ds1[m & 1], dq[m >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto run = [&](int32_t it, char* kt, char* vt, char* kn, char* vn) __attribute__((always_inline)) {
+        const NextTile nx = next_tile(tr, it + 1, a.k, a.v, a.n, a.heads, head, kn, vn);
+        if (wave_has_rows) {
+            const int32_t j0 = tiles::tile_at(tr, it) * TR;
+            const bool full = __builtin_amdgcn_ballot_w64(!row_ok || ((lo0 <= j0) & (j0 + TR <= hi0)) ||
+                                                          ((lo1 <= j0) & (j0 + TR <= hi1))) == ~0ull;
+            step(full, j0, kt, vt, nx);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) next_piece(nx, lm, wave, i);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     };
 
     if (tr.total > 0) {
-        load(0, k0, v0);
+        const NextTile first = next_tile(tr, 0, a.k, a.v, a.n, a.heads, head, k0, v0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) next_piece(first, lm, wave, i);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     for (int32_t it = 0; it < tr.total; it += 2) {
-        if (it + 1 < tr.total) load(it + 1, k1, v1);
-        if (wave_has_rows) step(it, k0, v0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        run(it, k0, v0, k1, v1);
         if (it + 1 >= tr.total) break;
-        if (it + 2 < tr.total) load(it + 2, k0, v0);
-        if (wave_has_rows) step(it + 1, k1, v1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        run(it + 1, k1, v1, k0, v0);
     }
 
     if (row_ok) {
