@@ -506,7 +506,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int32_t key = c0 + wave * 32 + l32;
     const bool key_ok = key < a.n;
     const bool wave_has_keys = c0 + wave * 32 < a.n;
-    const tiles::TileRanges tr = col_tile_ranges(a.mask, a.n, c0, c0 + BR);
+    const tiles::TileRanges tr = uniform(col_tile_ranges(a.mask, a.n, c0, c0 + BR));
     int32_t lo0, hi0, lo1, hi1;
     col_ranges(a.mask, a.n, key, lo0, hi0, lo1, hi1);
 
@@ -523,6 +523,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     }
     const float cs = a.scale * kLog2e;
     const Frag fr = frag_offsets(lane);
+    const RowOff ro = row_offsets(fr);
     const TileLoad lm = tile_load_map(threadIdx.x, (uint32_t)(a.heads * ROWB));
 #pragma unroll
     for (int i = 0; i < BR / TR; ++i)
@@ -550,97 +551,138 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
             rowv[buf][1][threadIdx.x] = rv_d;
         }
     };
-    auto load = [&](int32_t it, char* qt, char* dt) __attribute__((always_inline)) {
-        const int32_t i0 = tiles::tile_at(tr, it) * TR;
-        load_tile((const char*)a.q, i0, a.n, a.heads, head, lm, (char LDS_AS*)qt, wave);
-        load_tile((const char*)a.dout, i0, a.n, a.heads, head, lm, (char LDS_AS*)dt, wave);
-    };
-    auto step = [&](int32_t it, const char* qt_, const char* dt_, int buf) __attribute__((always_inline)) {
+
+    // One query tile as one stream of 64 MFMAs, per 32-row half qb:
+    //   S   = Q K^T               (8; Q rows from LDS, K^T in registers)
+    //   P   = 2^(S cs - lse)       VALU, rounded to bf16
+    //   dV^T += dO^T P            (8; dO^T from transposing reads)
+    //   dP  = dO V^T              (8; dO rows and this wave's V rows from LDS)
+    //   dS  = P (dP - D)           VALU, in bf16
+    //   dK^T += Q^T dS            (8; Q^T from transposing reads)
+    // Every fragment is read two MFMAs ahead of its use, across the VALU steps
+    // too; a scheduling fence after each MFMA keeps this written order, and the
+    // next tile's direct loads are spread over the first S group.  The two
+    // halves run as a loop (not unrolled): the mask branch of an unrolled pair
+    // costs more registers than the kernel has.
+    auto step = [&](bool full, int32_t i0, const char* qt_, const char* dt_, int buf, const NextTile& nx)
+                    __attribute__((always_inline)) {
         const char LDS_AS* qt = (const char LDS_AS*)qt_;
         const char LDS_AS* dt = (const char LDS_AS*)dt_;
-        const int32_t i0 = tiles::tile_at(tr, it) * TR;
-        const bool full = __builtin_amdgcn_ballot_w64(
-                              !key_ok || ((lo0 <= i0) & (i0 + TR <= hi0)) || ((lo1 <= i0) & (i0 + TR <= hi1))) ==
-                          ~0ull;
+        bf16x8 fa[32], fb[32];  // fragments of MFMA n of a half (fb: the dP group's B operand)
+        auto fetch = [&](int qb, int n) __attribute__((always_inline)) {
+            const int ph = (n >> 3) & 3, i = n & 7;
+            if (ph == 0) {
+                fa[n] = rows_frag(qt, ro, qb, i);
+            } else if (ph == 1) {
+                fa[n] = tr_frag(dt, fr, qb, i >> 1, i & 1);
+            } else if (ph == 2) {
+                fa[n] = rows_frag(dt, ro, qb, i);
+                fb[n] = rows_frag(vw, ro, 0, i);
+            } else {
+                fa[n] = tr_frag(qt, fr, qb, i >> 1, i & 1);
+            }
+        };
+        f32x16 s, dp;
+        bf16x8 pb[2], dsb[2];
+        auto weights = [&](int qb) __attribute__((always_inline)) {
+            if (!full) {
+                // rows of the half that may not see this lane's key: score -inf.
+                // Register r holds row i0 + 32 qb + 4 h + c(r), c(r) = 8 (r/4) + r%4;
+                // the test (i - lo) < (hi - lo) (unsigned) is one add of c(r) to a
+                // per-step base (pinned, so that the compiler does not keep a
+                // hoisted copy of base + c(r) for every r across the loop).
+                int32_t b0 = i0 + qb * 32 + 4 * h - lo0, b1 = i0 + qb * 32 + 4 * h - lo1;
+                asm volatile("" : "+v"(b0), "+v"(b1));
+                const uint32_t n0 = (uint32_t)(hi0 - lo0), n1 = (uint32_t)(hi1 - lo1);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int32_t c = 8 * (r >> 2) + (r & 3);
+                    const bool ok = ((uint32_t)(b0 + c) < n0) | ((uint32_t)(b1 + c) < n1);
+                    s[r] = ok ? s[r] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // registers 4g .. 4g+3 hold rows 32 qb + 16 (g/2) + 8 (g%2) + 4 h + {0..3}
+                const f32x4 l4 = *(const f32x4*)&rowv[buf][0][qb * 32 + 8 * g + 4 * h];
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    pb[g >> 1][4 * (g & 1) + w] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + w], cs, -l4[w]));
+            }
+            pin(pb[0]);
+            pin(pb[1]);
+        };
+        auto dscores = [&](int qb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 d4 = *(const f32x4*)&rowv[buf][1][qb * 32 + 8 * g + 4 * h];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int e = 4 * (g & 1) + w;
+                    dsb[g >> 1][e] = (__bf16)((float)pb[g >> 1][e] * (dp[4 * g + w] - d4[w]));
+                }
+            }
+            pin(dsb[0]);
+            pin(dsb[1]);
+        };
 #pragma nounroll
         for (int qb = 0; qb < 2; ++qb) {
-            // P first (then its fp32 scores are dead), dV^T += dO^T P; then dP and
-            // dS = P (dP - D) from the bf16 P, dK^T += Q^T dS: fewer live registers
-            f32x16 s = f32x16{};
+        fetch(qb, 0);
+        fetch(qb, 1);
 #pragma unroll
-            for (int ds = 0; ds < 8; ++ds) s = mfma(rows_frag(qt, fr, qb, ds), kf[ds], s);
+        for (int n = 0; n < 32; ++n) {
+            const int ph = (n >> 3) & 3, i = n & 7;
+            if (n + 2 < 32) fetch(qb, n + 2);
+            if (ph == 0) {
+                if (i == 0) s = f32x16{};
+                s = mfma(fa[n], kf[i], s);
+                if (qb == 0 && (i & 1)) next_piece(nx, lm, wave, i >> 1);
+            } else if (ph == 1) {
+                dv[i >> 1] = mfma(fa[n], pb[i & 1], dv[i >> 1]);
+            } else if (ph == 2) {
+                if (i == 0) dp = f32x16{};
+                dp = mfma(fa[n], fb[n], dp);
+            } else {
+                dk[i >> 1] = mfma(fa[n], dsb[i & 1], dk[i >> 1]);
+            }
             __builtin_amdgcn_sched_barrier(0);
-            bf16x8 pb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    // registers 8t + 4u .. + 3 hold rows 32 qb + 16 t + 8 u + 4 h + {0..3}
-                    const int rr = qb * 32 + 16 * t + 8 * u + 4 * h;
-                    const f32x4 l4 = *(const f32x4*)&rowv[buf][0][rr];
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * t + 4 * u + w], cs, -l4[w]));
-                        if (!full) {
-                            const uint32_t ok = tiles::in_range(i0 + rr + w, lo0, hi0) |
-                                                tiles::in_range(i0 + rr + w, lo1, hi1);
-                            p = ok ? p : 0.0f;
-                        }
-                        pb[t][4 * u + w] = (__bf16)p;
-                    }
-                }
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) dv[db] = mfma(tr_frag(dt, fr, qb, db, t), pb[t], dv[db]);
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 dp = f32x16{};
-#pragma unroll
-            for (int ds = 0; ds < 8; ++ds) dp = mfma(rows_frag(dt, fr, qb, ds), rows_frag(vw, fr, 0, ds), dp);
-            bf16x8 dsb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int rr = qb * 32 + 16 * t + 8 * u + 4 * h;
-                    const f32x4 d4 = *(const f32x4*)&rowv[buf][1][rr];
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        dsb[t][4 * u + w] = (__bf16)((float)pb[t][4 * u + w] * (dp[8 * t + 4 * u + w] - d4[w]));
-                }
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) dk[db] = mfma(tr_frag(qt, fr, qb, db, t), dsb[t], dk[db]);
+            if (i == 7 && ph == 0) weights(qb);
+            if (i == 7 && ph == 2) dscores(qb);
             __builtin_amdgcn_sched_barrier(0);
         }
+        }
+    };
+    auto run = [&](int32_t it, char* qt, char* dt, char* qn, char* dn, int buf) __attribute__((always_inline)) {
+        const NextTile nx = next_tile(tr, it + 1, a.q, a.dout, a.n, a.heads, head, qn, dn);
+        const bool more = it + 1 < tr.total;
+        if (more) fetch_rows(it + 1);
+        if (wave_has_keys) {
+            const int32_t i0 = tiles::tile_at(tr, it) * TR;
+            const bool full = __builtin_amdgcn_ballot_w64(!key_ok || ((lo0 <= i0) & (i0 + TR <= hi0)) ||
+                                                          ((lo1 <= i0) & (i0 + TR <= hi1))) == ~0ull;
+            step(full, i0, qt, dt, buf, nx);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) next_piece(nx, lm, wave, i);
+        }
+        if (more) store_rows(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     };
 
     if (tr.total > 0) {
-        load(0, q0, d0);
+        const NextTile first = next_tile(tr, 0, a.q, a.dout, a.n, a.heads, head, q0, d0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) next_piece(first, lm, wave, i);
         fetch_rows(0);
         store_rows(0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     for (int32_t it = 0; it < tr.total; it += 2) {
-        if (it + 1 < tr.total) {
-            load(it + 1, q1, d1);
-            fetch_rows(it + 1);
-        }
-        if (wave_has_keys) step(it, q0, d0, 0);
-        if (it + 1 < tr.total) store_rows(1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        run(it, q0, d0, q1, d1, 0);
         if (it + 1 >= tr.total) break;
-        if (it + 2 < tr.total) {
-            load(it + 2, q0, d0);
-            fetch_rows(it + 2);
-        }
-        if (wave_has_keys) step(it + 1, q1, d1, 1);
-        if (it + 2 < tr.total) store_rows(0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        run(it + 1, q1, d1, q0, d0, 1);
     }
 
     if (key_ok) {
