@@ -719,6 +719,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         }
 
         if (wave_has_rows) {
+            // Wave priority falls as the step progresses (3 at the start, 2 and 1
+            // within [A], 0 halfway through [B]): of the two waves of a SIMD the one
+            // behind keeps the higher priority, so both reach the barrier together.
+            // (By age alone, the older wave finished ~500 cycles early every step
+            // and waited while the younger one ran alone.)
+            __builtin_amdgcn_s_setprio(3);
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
             // [A] S^T(it+1) = K(it+1) Q^T on the matrix core, next to the second
             //     half of this tile's weights (pf1) on the VALU.  The order is
@@ -752,6 +758,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
                         if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
                     }
                     sn1 = mfma8(ka8[ks][1], qf8[ks], sn1);
+                    if (ks == kDS8 - 1) __builtin_amdgcn_s_setprio(1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else if constexpr (!LAST) {
@@ -779,6 +786,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
                         if (idx < 8) e0[idx] = v; else e1[idx - 8] = v;
                     }
                     sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][1], qf[ds], sn1, 0, 0, 0);
+                    if (ds == 3) __builtin_amdgcn_s_setprio(2);
+                    if (ds == 7) __builtin_amdgcn_s_setprio(1);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
@@ -839,6 +848,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
                     constexpr int db = i / 4, t = (i / 2) % 2, kb = i % 2;
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[i % (VPF + 1)], kb ? pf1[t] : pf0[t], o[db],
                                                                     0, 0, 0);
+                    if constexpr (i == NPV / 2) __builtin_amdgcn_s_setprio(0);
                     if constexpr (!LAST) {
                         if constexpr (i < RMX) {  // row max of S^T(it+1), 32 / RMX values per slot
 #pragma unroll
