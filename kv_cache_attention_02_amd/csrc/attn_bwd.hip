@@ -393,6 +393,10 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
             }
         };
         bf16x8 ds0[2], ds1[2];
+        // wave priority falls as the tile progresses (3, 2 after A0, 1 after A1,
+        // 0 after B0): of the two waves of a SIMD the one behind keeps the
+        // higher priority, so both reach the barrier together
+        __builtin_amdgcn_s_setprio(3);
         // A0
         rows(0, 0);
         rows(0, 1);
@@ -408,6 +412,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // V0
+        __builtin_amdgcn_s_setprio(2);
         mask(0);
 #pragma unroll
         for (int g = 0; g < 4; ++g) dsg(g, ds0);
@@ -426,6 +431,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         mask(1);
+        __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
         // B0 beside V1
 #pragma unroll
@@ -437,6 +443,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
                 dsg(m >> 1, ds1);
                 pin(ds1[m >> 2]);
             }
+            if (m == 7) __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
         // B1
@@ -625,6 +632,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
             pin(dsb[0]);
             pin(dsb[1]);
         };
+        // wave priority falls as the tile progresses (3; 2 after the dV group of
+        // half 0; 1 after half 0; 0 after the dV group of half 1), as in dQ
+        __builtin_amdgcn_s_setprio(3);
 #pragma nounroll
         for (int qb = 0; qb < 2; ++qb) {
         fetch(qb, 0);
@@ -648,6 +658,11 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             if (i == 7 && ph == 0) weights(qb);
             if (i == 7 && ph == 2) dscores(qb);
+            if (i == 7 && ph == 1) {
+                if (qb) __builtin_amdgcn_s_setprio(0);
+                else __builtin_amdgcn_s_setprio(2);
+            }
+            if (i == 7 && ph == 3 && qb == 0) __builtin_amdgcn_s_setprio(1);
             __builtin_amdgcn_sched_barrier(0);
         }
         }
