@@ -83,12 +83,8 @@ __device__ __forceinline__ Frag frag_offsets(int lane) {
     return f;
 }
 
-// A operand from rows: rows 32 kb + l32, dims 16 ds + 8 h .. + 7
-__device__ __forceinline__ bf16x8 rows_frag(const char LDS_AS* tile, const Frag& f, int kb, int ds) {
-    return *(const bf16x8 LDS_AS*)(tile + kb * 32 * ROWB + f.base + (f.xr ^ (uint32_t)(32 * ds)));
-}
-
-// The eight row-read offsets base + (xr ^ 32 ds) as separate values: every
+// A operand from rows: rows 32 kb + l32, dims 16 ds + 8 h .. + 7.  The eight
+// row-read offsets base + (xr ^ 32 ds) are kept as separate values: every
 // read is then one of them plus a compile-time offset (the tile object and the
 // row block fold into the instruction's immediate).
 struct RowOff {
@@ -159,7 +155,7 @@ __device__ __forceinline__ void load_tile(const char* src, int32_t r0, int32_t n
                                           const TileLoad& m, char LDS_AS* tile, int wave) {
     const uint32_t row_stride = (uint32_t)heads * ROWB;
     const int32_t valid = max(0, min(TR, n - r0));
-    const __amdgpu_buffer_rsrc_t r = rsrc(src + ((size_t)r0 * heads + head) * ROWB, (uint32_t)valid * row_stride);
+    const __amdgpu_buffer_rsrc_t r = rsrc_uniform(src + ((size_t)r0 * heads + head) * ROWB, (uint32_t)valid * row_stride);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16(r, m.off[i], tile + i * (TILEB / 2) + wave * 1024);
 }
