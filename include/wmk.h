@@ -181,7 +181,8 @@ size_t wmk_attention_qk8_workspace_bytes(const wmk_head_desc* hd, int32_t q_toke
  * scores S = Q K^T come from FP8 (OCP e4m3) operands with one fp32 scale per
  * block -- the precision variant of the attention step ("LingBot-World-
  * Infinity" acceleration table: an INT8-QK^T SageAttention kernel replaces
- * FlashAttention-2; this build quantizes to FP8 for the CDNA4 matrix cores).
+ * FlashAttention-2; here the operands are quantized to FP8 for the CDNA4 matrix
+ * cores).
  * Per head, Q is cut into blocks of 32 rows and the keys -- cache slots in
  * slot order, then the segments -- into tiles of 64; per block, in fp32:
  * scale = max|x| / 448, code = e4m3(clamp(x * 448 / max|x|, +-448)), nearest
