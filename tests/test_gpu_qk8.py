@@ -2,7 +2,7 @@
 the e4m3 codes and block scales of Q and K (read back from the workspace)
 bit for bit against the oracle's quantizer, the outputs against the oracle's
 quantized attention (bf16 bounds) on small ragged shapes and sampled rows at
-832x464, and the quantization error against the exact attention (the looser
+832x464 and 720p, and the quantization error against the exact attention (the looser
 bound of the quantized path)."""
 import math
 
@@ -119,6 +119,44 @@ def test_qk8_832x464(wmk):
             BF16_REL_L2, f"{len(rows)} rows vs quantized oracle")
     compare(got, oracle.chunk_attention(cm, q, [(k, v)], 1 / math.sqrt(D), rows=rows), QK8_MAX_ABS_VS_EXACT,
             QK8_REL_L2_VS_EXACT, f"{len(rows)} rows vs exact attention")
+    cache.close()
+
+
+def test_qk8_720p_sampled_heads(wmk):
+    """The 720p step (tpf 3600, 24 heads, 14 resident frames + the 14 400-token chunk:
+    64 800 keys) through the FP8 path.  Quantization and attention are per head, so the
+    oracle works on three heads: their codes and scales bit for bit, and sampled rows
+    against the quantized oracle and the exact attention."""
+    import torch
+    S, W, cf, tpf, H, D = 6, 8, 4, 3600, 24, 128
+    heads = [0, 13, 23]
+    cache, cm = _filled(wmk, S, W, cf, tpf, H, D, 5, seed=46)
+    nq = cf * tpf
+    q, k, v = (host((nq, H, D), seed=47, kind=t) for t in (synth.Q, synth.K, synth.V))
+    nk = 14 * tpf + nq
+    ws = torch.zeros(wmk.qk8_workspace_bytes(H, nq, nk), dtype=torch.uint8, device="cuda")
+    say("qk8 720p")
+    out = wmk.chunk_attention_qk8(cache, 0, to_dev(q), [(to_dev(k), to_dev(v))], ws=ws)
+    torch.cuda.synchronize()
+    k_seq, v_seq = oracle.kernel_key_sequence(cm, [(k, v)])
+    assert k_seq.shape[0] == nk
+    k8, ks, q8, qs = _regions(ws, H, nq, nk)
+    q32 = oracle.widen(q)[:, heads]
+    kc, kss = oracle.quantize_e4m3_blocks(k_seq[:, heads], 64)
+    qc, qss = oracle.quantize_e4m3_blocks(q32, 32)
+    np.testing.assert_array_equal(ks[:, heads].view(np.uint32), kss.view(np.uint32))
+    np.testing.assert_array_equal(qs[:, heads].view(np.uint32), qss.view(np.uint32))
+    np.testing.assert_array_equal(k8[:, heads], kc)
+    np.testing.assert_array_equal(q8[:, heads], qc)
+    rows = sample_rows(nq, np.random.default_rng(10), k=12, tile=256)
+    got = from_dev(out)[rows][:, heads]
+    qd = oracle.dequantize_e4m3_blocks(qc, qss, nq)[rows]
+    kd = oracle.dequantize_e4m3_blocks(kc, kss, nk)
+    scale = 1 / math.sqrt(D)
+    compare(got, oracle.attend_dense_f64(qd, kd, v_seq[:, heads], scale), BF16_MAX_ABS, BF16_REL_L2,
+            f"{len(rows)} rows x {len(heads)} heads vs quantized oracle")
+    exact = oracle.attend_dense_f64(q32[rows], k_seq[:, heads], v_seq[:, heads], scale)
+    compare(got, exact, QK8_MAX_ABS_VS_EXACT, QK8_REL_L2_VS_EXACT, f"{len(rows)} rows vs exact attention")
     cache.close()
 
 
