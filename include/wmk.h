@@ -127,11 +127,22 @@ wmk_status wmk_cache_init(const wmk_cache_desc* d, void* k_dev, void* v_dev, siz
 /* Free the host handle (not the caller's buffers).  NULL is accepted. */
 void wmk_cache_destroy(wmk_cache* c);
 
-/* Append n_frames finalized frames to `layer` and evict in the same step.
+/* Append n_frames finalized frames to `layer` and evict in the same step:
+ * the cache keeps its sink frames at the front for good and slides a window of
+ * recent frames, discarding the oldest non-sink frame once the window is full
+ * ("LingBot-World-Infinity: The Open-Source World Model That Refuses to
+ * Forget", "How the cache keeps the world alive"; the simplified loop of "The
+ * trick: treat video like a causal stream" -- evict old state, keep the
+ * anchors, step, append -- with evict and append done here as one call after a
+ * chunk is finalized).  In the native model the frames appended are the
+ * recently finalized outputs the self-attention reads next to the initial
+ * observation ("Westlake AGI Lab's 'World in World' Steers Frozen Video
+ * Models", second paragraph).
  * k_new and v_new are [n_frames * tokens_per_frame][heads][head_dim] in the
- * cache dtype.  Frame f (global append order) lands in slot f if f < S, else
- * in slot S + (f - S) mod W, overwriting -- and so evicting -- frame f - W.
- * Frames that this same call would overwrite (only when n_frames > W) are not
+ * cache dtype, device memory owned by the caller and only read here.  Frame f
+ * (global append order) lands in slot f if f < S, else in slot
+ * S + (f - S) mod W, overwriting -- and so evicting -- frame f - W.  Frames
+ * that this same call would overwrite (only when n_frames > W) are not
  * written.  Bits are copied exactly.  The frame counter advances on enqueue.
  * Errors: NULL -> WMK_ERR_NULL; layer outside [0, num_layers) -> WMK_ERR_RANGE;
  * n_frames <= 0 -> WMK_ERR_SHAPE; misaligned -> WMK_ERR_ALIGN; launch refused
@@ -139,10 +150,16 @@ void wmk_cache_destroy(wmk_cache* c);
 wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new, const void* v_new,
                                   int32_t n_frames, hipStream_t stream);
 
-/* Host-side view of a layer's slots: frame_of_slot[S + W] receives the frame
+/* Host-side view of a layer's slots, the bookkeeping of the sink + window
+ * cache ("How the cache keeps the world alive": sinks kept at the front, the
+ * window sliding behind them; "World in World", second paragraph: 6 anchor and
+ * 8 recent-frame slots beside the 4 of the current chunk in the native model).
+ * frame_of_slot[S + W] (a host array owned by the caller) receives the frame
  * held by each slot (-1 when empty) and *frames_appended the layer's counter
  * (either output pointer may be NULL).  Resident frames always fill the slot
- * prefix [0, valid).  No GPU work. */
+ * prefix [0, valid).  No GPU work, no synchronization: computed from the host
+ * counter alone.  Errors: NULL c -> WMK_ERR_NULL; layer out of range ->
+ * WMK_ERR_RANGE. */
 wmk_status wmk_cache_slots(const wmk_cache* c, int32_t layer, int64_t* frame_of_slot, int64_t* frames_appended);
 
 /* Bytes of optional scratch that lets the attention calls below split the last,
@@ -179,10 +196,10 @@ size_t wmk_attention_qk8_workspace_bytes(const wmk_head_desc* hd, int32_t q_toke
 
 /* Chunk attention with a quantized QK^T: as wmk_chunk_attention, but the
  * scores S = Q K^T come from FP8 (OCP e4m3) operands with one fp32 scale per
- * block -- the precision variant of the attention step ("LingBot-World-
- * Infinity" acceleration table: an INT8-QK^T SageAttention kernel replaces
- * FlashAttention-2; here the operands are quantized to FP8 for the CDNA4 matrix
- * cores).
+ * block -- the precision variant of the attention step (LingBot-World 2.0
+ * speed-up page, step table, "Attention" row: an INT8-QK^T SageAttention
+ * kernel replaces FlashAttention-2; roofline table, "SageAttention" row; here
+ * the operands are quantized to FP8 for the CDNA4 matrix cores).
  * Per head, Q is cut into blocks of 32 rows and the keys -- cache slots in
  * slot order, then the segments -- into tiles of 64; per block, in fp32:
  * scale = max|x| / 448, code = e4m3(clamp(x * 448 / max|x|, +-448)), nearest
@@ -207,8 +224,9 @@ wmk_status wmk_chunk_attention_qk8(const wmk_cache* c, int32_t layer, const wmk_
  * host array of global frame indices, any order, as reported by
  * wmk_cache_slots) are attended; the others stay in the cache, untouched, for
  * later calls.  This is the per-call choice of retained history of a dynamic
- * KV-cache scheduler ("LingBot-World-Infinity" overview, deployment: retained
- * history adapted to the current control signal).  Temporary auxiliary KV
+ * KV-cache scheduler ("Infinite Worlds with Versatile Interactions",
+ * deployment paragraph: retained history adapted to the current control
+ * signal).  Temporary auxiliary KV
  * blocks of the current chunk ("World in World", second paragraph: extra
  * evidence for the current chunk, dropped once it is finalized) are passed as
  * segments and never appended.  n_keep = 0 attends the segments only.  The
@@ -233,8 +251,7 @@ wmk_status wmk_chunk_attention_retained(const wmk_cache* c, int32_t layer, const
  * [head_dim] in the dtype of hd.  Errors as for wmk_chunk_attention, plus
  * bidir_block outside {0, 1} or a non-positive field -> WMK_ERR_SHAPE. */
 wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
-                              const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream);
+                              const void* v, void* out, float scale, hipStream_t stream);
 
 /* MoBA forward for training: wmk_moba_attention plus the per-row log-sum-exp
  * the backward needs.  lse is [num_heads][n] fp32 (n = sequence length), lse =

@@ -71,7 +71,7 @@ _SIGNATURES = {
                                                     ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P,
                                                     ctypes.c_float, _P, ctypes.c_size_t, _P]),
     "wmk_moba_attention": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P, _P, _P,
-                                          _P, ctypes.c_float, _P, ctypes.c_size_t, _P]),
+                                          _P, ctypes.c_float, _P]),
     "wmk_moba_attention_train": (ctypes.c_int, [ctypes.POINTER(wmk_moba_desc), ctypes.POINTER(wmk_head_desc), _P,
                                                 _P, _P, _P, _P, ctypes.c_float, _P]),
     "wmk_moba_backward_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_moba_desc),
@@ -152,16 +152,56 @@ def _ptr(t):
 _workspaces = {}
 
 
-def workspace(device, nbytes):
-    """A per-device scratch buffer of at least nbytes (grown on demand, kept for reuse)."""
+def workspace(device, nbytes, stream=None):
+    """A scratch buffer of at least nbytes for calls on `stream` (default: the
+    current stream of `device`), grown on demand and kept for reuse.  One buffer
+    per (device, stream): calls on different streams never share scratch, and a
+    buffer is allocated on the stream that uses it, so when it is replaced the
+    caching allocator reuses its memory only behind that stream's queued work."""
     torch = _torch()
     dev = torch.device(device)
-    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    s = torch.cuda.current_stream(idx) if stream is None else stream
+    key = (idx, s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=torch.device("cuda", idx))
         _workspaces[key] = ws
     return ws
+
+
+def _check_tensor(name, t, *, dtype=None, device=None, rows=None, heads=None, head_dim=None, ndim=3):
+    """Raise ValueError unless t is a contiguous tensor of the given dtype, device and
+    shape [rows][heads][head_dim] (None: any)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, has shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    want = (rows, heads, head_dim)
+    for i, w in enumerate(want[:ndim]):
+        if w is not None and t.shape[i] != w:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                             f"{tuple(x if x is not None else '*' for x in want[:ndim])}")
+
+
+def _on_device(**tensors):
+    """Raise ValueError unless every tensor is device memory (checked after the shapes)."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor (is on {t.device})")
+
+
+def _check_like(name, t, ref, rows=None):
+    _check_tensor(name, t, dtype=ref.dtype, device=ref.device, rows=ref.shape[0] if rows is None else rows,
+                  heads=ref.shape[1], head_dim=ref.shape[2])
 
 
 class Cache:
@@ -193,8 +233,18 @@ class Cache:
         return self._h
 
     def append_evict(self, layer, k_new, v_new, n_frames=None, stream=None):
+        """Append the finalized frames k_new/v_new ([n_frames * tokens_per_frame][H][D]) to `layer`."""
+        tpf = self.desc.tokens_per_frame
+        _check_tensor("k_new", k_new, dtype=self.dtype, device=self.k.device, heads=self.desc.num_heads,
+                      head_dim=self.desc.head_dim)
         if n_frames is None:
-            n_frames = k_new.shape[0] // self.desc.tokens_per_frame
+            if k_new.shape[0] % tpf:
+                raise ValueError(f"k_new has {k_new.shape[0]} rows, not a whole number of {tpf}-token frames")
+            n_frames = k_new.shape[0] // tpf
+        if k_new.shape[0] != n_frames * tpf:
+            raise ValueError(f"k_new has {k_new.shape[0]} rows, {n_frames} frames need {n_frames * tpf}")
+        _check_like("v_new", v_new, k_new)
+        _on_device(k_new=k_new)
         _check(load().wmk_cache_append_evict(self._h, layer, _ptr(k_new), _ptr(v_new), n_frames,
                                              _stream_ptr(stream)))
 
@@ -217,6 +267,24 @@ class Cache:
             pass
 
 
+def _check_cache(cache, q):
+    if cache is None:
+        return
+    if q.dtype != cache.dtype or q.device != cache.k.device or q.shape[1:] != cache.k.shape[3:]:
+        raise ValueError(f"q ({q.dtype}, {q.device}, heads x dim {tuple(q.shape[1:])}) does not match the cache "
+                         f"({cache.dtype}, {cache.k.device}, {tuple(cache.k.shape[3:])})")
+
+
+def _segments(segments, q):
+    """ctypes array of the (k, v) segments; each [n][H][D] like q."""
+    segs = (wmk_kv_segment * max(1, len(segments)))()
+    for i, (k, v) in enumerate(segments):
+        _check_tensor(f"segment {i} k", k, dtype=q.dtype, device=q.device, heads=q.shape[1], head_dim=q.shape[2])
+        _check_like(f"segment {i} v", v, k)
+        segs[i] = wmk_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[0])
+    return segs
+
+
 def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_workspace=True, stream=None,
                     keep_frames=None):
     """out[q_tokens][H][D] = attention of q over the resident frames of `layer` in `cache`
@@ -224,19 +292,21 @@ def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_work
     keep_frames: attend only these resident frames (global frame indices);
     None attends all of them."""
     torch = _torch()
+    _check_tensor("q", q)
     nq, H, D = q.shape
+    _check_cache(cache, q)
     if out is None:
         out = torch.empty_like(q)
+    _check_like("out", out, q)
     hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
-    segs = (wmk_kv_segment * max(1, len(segments)))()
-    for i, (k, v) in enumerate(segments):
-        segs[i] = wmk_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[0])
+    segs = _segments(segments, q)
+    _on_device(q=q)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     ws, wsb = ctypes.c_void_p(0), 0
     if use_workspace:
         wsb = load().wmk_attention_workspace_bytes(ctypes.byref(hd), nq)
         if wsb:
-            w = workspace(q.device, wsb)
+            w = workspace(q.device, wsb, stream)
             ws, wsb = _ptr(w), w.numel()
     if keep_frames is None:
         _check(load().wmk_chunk_attention(cache.handle if cache is not None else None, layer, ctypes.byref(hd),
@@ -262,21 +332,25 @@ def chunk_attention_qk8(cache, layer, q, segments=(), out=None, scale=None, stre
     the workspace (its head then holds the quantized operands, see include/wmk.h); by
     default a cached one sized for every resident frame plus the segments."""
     torch = _torch()
+    _check_tensor("q", q)
     nq, H, D = q.shape
+    _check_cache(cache, q)
     if out is None:
         out = torch.empty_like(q)
+    _check_like("out", out, q)
     hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
-    segs = (wmk_kv_segment * max(1, len(segments)))()
-    kv = 0
-    for i, (k, v) in enumerate(segments):
-        segs[i] = wmk_kv_segment(k.data_ptr(), v.data_ptr(), k.shape[0])
-        kv += k.shape[0]
+    segs = _segments(segments, q)
+    kv = sum(k.shape[0] for k, _ in segments)
+    _on_device(q=q)
     if cache is not None:
         kv += (cache.desc.sink_frames + cache.desc.window_frames) * cache.desc.tokens_per_frame
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     if ws is None:
         wsb = load().wmk_attention_qk8_workspace_bytes(ctypes.byref(hd), nq, kv)
-        ws = workspace(q.device, wsb) if wsb else None
+        ws = workspace(q.device, wsb, stream) if wsb else None
+    elif not (isinstance(ws, torch.Tensor) and ws.dtype == torch.uint8 and ws.dim() == 1 and ws.is_contiguous()
+              and ws.device == q.device):
+        raise ValueError("ws must be a contiguous 1-d uint8 tensor on the device of q")
     wsp, wsb = (_ptr(ws), ws.numel()) if ws is not None else (ctypes.c_void_p(0), 0)
     _check(load().wmk_chunk_attention_qk8(cache.handle if cache is not None else None, layer, ctypes.byref(hd),
                                           _ptr(q), nq, segs, len(segments), _ptr(out), scale, wsp, wsb,
@@ -288,26 +362,44 @@ def moba_attention(q, k, v, *, tokens_per_frame, frames, chunk_frames, bidir_blo
                    stream=None):
     """MoBA-masked attention forward over [clean | noisy | block]."""
     torch = _torch()
+    _check_moba(q, k, v, tokens_per_frame, frames, bidir_block)
     n, H, D = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _check_like("out", out, q)
+    _on_device(q=q)
     hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
     md = wmk_moba_desc(tokens_per_frame, frames, chunk_frames, bidir_block)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(load().wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                     scale, None, 0, _stream_ptr(stream)))
+                                     scale, _stream_ptr(stream)))
     return out
+
+
+def _check_moba(q, k, v, tokens_per_frame, frames, bidir_block):
+    """q, k, v: [(2 + bidir_block) * frames * tokens_per_frame][H][D], alike."""
+    _check_tensor("q", q)
+    n = (2 + bidir_block) * frames * tokens_per_frame
+    if q.shape[0] != n:
+        raise ValueError(f"q has {q.shape[0]} rows; the MoBA sequence has (2 + {bidir_block}) * {frames} * "
+                         f"{tokens_per_frame} = {n}")
+    _check_like("k", k, q)
+    _check_like("v", v, q)
 
 
 def moba_attention_train(q, k, v, *, tokens_per_frame, frames, chunk_frames, bidir_block=1, out=None, lse=None,
                          scale=None, stream=None):
     """MoBA forward for training: returns (out, lse) with lse [H][n] fp32 (natural log)."""
     torch = _torch()
+    _check_moba(q, k, v, tokens_per_frame, frames, bidir_block)
     n, H, D = q.shape
     if out is None:
         out = torch.empty_like(q)
+    _check_like("out", out, q)
     if lse is None:
         lse = torch.empty((H, n), dtype=torch.float32, device=q.device)
+    _check_tensor("lse", lse, dtype=torch.float32, device=q.device, rows=H, heads=n, ndim=2)
+    _on_device(q=q)
     hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
     md = wmk_moba_desc(tokens_per_frame, frames, chunk_frames, bidir_block)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -320,13 +412,18 @@ def moba_attention_backward(q, k, v, out, dout, lse, *, tokens_per_frame, frames
                             scale=None, stream=None):
     """Gradients (dq, dk, dv) of sum(dout * out) for the MoBA-masked attention."""
     torch = _torch()
+    _check_moba(q, k, v, tokens_per_frame, frames, bidir_block)
     n, H, D = q.shape
+    _check_like("out", out, q)
+    _check_like("dout", dout, q)
+    _check_tensor("lse", lse, dtype=torch.float32, device=q.device, rows=H, heads=n, ndim=2)
+    _on_device(q=q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
     md = wmk_moba_desc(tokens_per_frame, frames, chunk_frames, bidir_block)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     wsb = load().wmk_moba_backward_workspace_bytes(ctypes.byref(md), ctypes.byref(hd))
-    ws = workspace(q.device, wsb)
+    ws = workspace(q.device, wsb, stream)
     _check(load().wmk_moba_attention_backward(ctypes.byref(md), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v),
                                               _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), scale,
                                               _ptr(ws), ws.numel(), _stream_ptr(stream)))
@@ -339,12 +436,18 @@ def cross_attention_train(q, k, v, *, chunk_q_tokens, env_tokens, local_tokens, 
     (rows [i * chunk_q_tokens, (i + 1) * chunk_q_tokens)) reads keys
     [0, env_tokens) and its own local prompt [env_tokens + i * local_tokens, +local_tokens)."""
     torch = _torch()
+    _check_tensor("q", q)
     nq, H, D = q.shape
     if chunk_q_tokens <= 0 or nq % chunk_q_tokens:
         raise ValueError(f"{nq} query tokens are not a whole number of chunks of {chunk_q_tokens}")
     chunks = nq // chunk_q_tokens
+    nk = env_tokens + chunks * local_tokens
+    _check_tensor("k", k, dtype=q.dtype, device=q.device, rows=nk, heads=H, head_dim=D)
+    _check_like("v", v, k)
+    _on_device(q=q)
     if out is None:
         out = torch.empty_like(q)
+    _check_like("out", out, q)
     hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
     xd = wmk_xattn_desc(chunk_q_tokens, chunks, env_tokens, local_tokens)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -352,7 +455,7 @@ def cross_attention_train(q, k, v, *, chunk_q_tokens, env_tokens, local_tokens, 
     if use_workspace:
         wsb = load().wmk_attention_workspace_bytes(ctypes.byref(hd), nq)
         if wsb:
-            w = workspace(q.device, wsb)
+            w = workspace(q.device, wsb, stream)
             ws, wsb = _ptr(w), w.numel()
     _check(load().wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(out), scale, ws, wsb, _stream_ptr(stream)))

@@ -337,8 +337,13 @@ size_t qk8_bytes(int32_t heads, int32_t q_tokens, int64_t kv_tokens, Qk8Bufs* b,
 
 // Chunk attention over the resident frames of `layer` (keep == NULL: all of
 // them; else the n_keep listed frames) plus the caller's segments.  The cache
-// part becomes one span per run of adjacent selected slots, in slot order:
-// softmax does not depend on the order of the keys.
+// part becomes one span per run of adjacent slots.  The plain paths visit the
+// slots in slot order (softmax does not depend on the order of the keys, and
+// the whole resident prefix is then one span); the FP8 path visits the
+// resident frames in time order -- sinks, then recent frames, oldest first --
+// because its 64-key scale blocks are cut along the key sequence, and in time
+// order that sequence, and so every block, depends only on which frames are
+// resident, not on where the ring has wrapped.
 wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t* keep, int32_t n_keep,
                                 const wmk_head_desc* hd, const void* q, int32_t q_tokens, const wmk_kv_segment* seg,
                                 int32_t n_seg, void* out, float scale, void* workspace, size_t workspace_bytes,
@@ -383,20 +388,31 @@ wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t
                 sel[slot] = 1;
             }
         }
+        // the selected slots in visiting order
+        std::vector<int32_t> order;
+        if (qk8) {
+            auto visit = [&](int64_t f) {
+                if (sel[slot_of(d, f)]) order.push_back((int32_t)slot_of(d, f));
+            };
+            for (int64_t f = 0; f < std::min<int64_t>(F, d.sink_frames); ++f) visit(f);
+            for (int64_t f = std::max<int64_t>(d.sink_frames, F - d.window_frames); f < F; ++f) visit(f);
+        } else {
+            for (int32_t a = 0; a < slots; ++a)
+                if (sel[a]) order.push_back(a);
+        }
         const size_t base = (size_t)layer * c->layer_bytes;
-        for (int32_t a = 0; a < slots;) {
-            if (!sel[a]) { ++a; continue; }
-            int32_t b = a;
-            while (b < slots && sel[b]) ++b;
+        for (size_t i = 0; i < order.size();) {
+            size_t j = i + 1;
+            while (j < order.size() && order[j] == order[j - 1] + 1) ++j;
             if (n + n_seg >= wmk::kMaxSeg)
                 return fail(WMK_ERR_CAPACITY, "retained frames form more than %d runs of adjacent slots with %d segments",
                             wmk::kMaxSeg - n_seg, n_seg);
-            call.kv.k[n] = c->k + base + (size_t)a * c->frame_bytes;
-            call.kv.v[n] = c->v + base + (size_t)a * c->frame_bytes;
-            total += (int64_t)(b - a) * d.tokens_per_frame;
+            call.kv.k[n] = c->k + base + (size_t)order[i] * c->frame_bytes;
+            call.kv.v[n] = c->v + base + (size_t)order[i] * c->frame_bytes;
+            total += (int64_t)(j - i) * d.tokens_per_frame;
             call.kv.end[n] = (int32_t)total;  // < 2^31: the cache size check bounds a layer's tokens
             ++n;
-            a = b;
+            i = j;
         }
     }
     for (int i = 0; i < n_seg; ++i) {
@@ -625,13 +641,11 @@ wmk_status wmk_chunk_attention_retained(const wmk_cache* c, int32_t layer, const
 }
 
 wmk_status wmk_moba_attention(const wmk_moba_desc* m, const wmk_head_desc* hd, const void* q, const void* k,
-                              const void* v, void* out, float scale, void* workspace, size_t workspace_bytes,
-                              hipStream_t stream) {
+                              const void* v, void* out, float scale, hipStream_t stream) {
     wmk::AttnCall call;
     const wmk_status s = moba_call(m, hd, q, k, v, out, scale, call);
     if (s != WMK_OK) return s;
-    (void)workspace;  // MoBA q-tiles differ in cost: longest first, no split tail
-    (void)workspace_bytes;
+    // MoBA q-tiles differ in cost: they run longest first and need no split tail
     return run_attention(call, hd->dtype, nullptr, 0, stream);
 }
 

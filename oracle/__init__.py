@@ -28,9 +28,14 @@ Sources (cited by page title and section):
   inference one chunk at a time; in training every chunk of a sequence at
   once, under the causal cross-attention mask).
 
-* "LingBot-World-Infinity" overview, deployment: a dynamic KV-cache scheduler
-  adapts the retained history to the current control signal (here: a call
-  attends a chosen subset of the resident frames).
+* "Infinite Worlds with Versatile Interactions", deployment paragraph: a
+  dynamic KV-cache scheduler adapts the retained history to the current
+  control signal (here: a call attends a chosen subset of the resident
+  frames).
+* LingBot-World 2.0 speed-up page (kaarelkaarelson.com/lingbot), step table
+  ("Attention" row: FlashAttention-2 replaced by SageAttention 2.2, a
+  quantized-QK^T kernel) and roofline table ("SageAttention" row): the
+  precision variant of the attention step.
 
 Readings where the pages are silent (all stated once more in the design notes):
 sinks and window are counted in latent frames; the window excludes the current
@@ -343,13 +348,15 @@ def cross_attention_train(q, k, v, chunk_q_tokens, env_tokens, local_tokens, sca
 
 
 # --------------------------------------------------------------------------------------------
-# Quantized QK^T: FP8 e4m3 codes with one fp32 scale per block (the precision-variant of the
-# attention step; "LingBot-World-Infinity" acceleration table: SageAttention 2.2 replaces
-# FlashAttention-2 with a quantized QK^T).  The pages fix no format or block shape; the readings
-# here: OCP e4m3 (largest finite 448), round to nearest even, symmetric absmax scaling per
-# (block of rows, head) -- 32 query rows, 64 keys -- with no smoothing; K blocks are 64
-# consecutive keys of the key sequence in the order the kernel reads it (cache slots in slot
-# order, then the segments); P and V stay bf16/fp32 as in the plain path.
+# Quantized QK^T: FP8 e4m3 codes with one fp32 scale per block (the precision variant of the
+# attention step; LingBot-World 2.0 speed-up page, step table "Attention" row: SageAttention 2.2,
+# a quantized-QK^T kernel, replaces FlashAttention-2; roofline table "SageAttention" row).  The
+# pages fix no format or block shape; the readings here: OCP e4m3 (largest finite 448), round to
+# nearest even, symmetric absmax scaling per (block of rows, head) -- 32 query rows, 64 keys --
+# with no smoothing; K blocks are 64 consecutive keys of the key sequence in time order (the
+# resident frames oldest first -- sinks, then the recent window -- then the segments), so which
+# keys share a scale depends only on the resident frames, never on where the ring buffer wraps;
+# P and V stay bf16/fp32 as in the plain path.
 # --------------------------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
@@ -431,15 +438,15 @@ def attend_dense_f64(q, k, v, scale):
     return out
 
 
-def kernel_key_sequence(cache, segments):
-    """Keys and values in the order the kernel reads them: the filled cache slots in slot
-    order, then each segment."""
+def qk8_key_sequence(cache, segments):
+    """Keys and values in the order the 64-key scale blocks are cut along: the resident
+    frames in time order (the sinks, then the recent window, oldest first), then each
+    segment."""
     ks, vs = [], []
     if cache is not None:
-        valid = valid_slots(cache.F, cache.S, cache.W)
-        kb, vb = cache.slot_buffers()
-        ks.append(kb[:valid].reshape(-1, cache.H, cache.D))
-        vs.append(vb[:valid].reshape(-1, cache.H, cache.D))
+        kc, vc = cache.logical_kv()
+        ks.append(kc)
+        vs.append(vc)
     for k, v in segments:
         ks.append(np.asarray(k))
         vs.append(np.asarray(v))
@@ -448,9 +455,9 @@ def kernel_key_sequence(cache, segments):
 
 def chunk_attention_qk8(cache, q, segments, scale, rows=None):
     """Chunk attention with the FP8-quantized QK^T: Q quantized in blocks of 32 rows, K in
-    blocks of 64 keys of the kernel's key sequence, softmax and P V exact (fp64) on the
+    blocks of 64 keys of the time-ordered key sequence, softmax and P V exact (fp64) on the
     dequantized scores.  ``rows`` selects query rows (default: all).  Returns fp64."""
-    k_all, v_all = kernel_key_sequence(cache, segments)
+    k_all, v_all = qk8_key_sequence(cache, segments)
     q32 = widen(q)
     qc, qs = quantize_e4m3_blocks(q32, 32)
     kc, ks = quantize_e4m3_blocks(k_all, 64)

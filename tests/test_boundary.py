@@ -269,7 +269,7 @@ def _oracle_qtile_cost(qt, tpf, frames, cf, bq, bk=64):
 def test_moba_launch_order_is_longest_first(lib, dry, tpf, frames, cf):
     hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
     md = wmk.wmk_moba_desc(tpf, frames, cf, 1)
-    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088, None, 0,
+    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088,
                                   None) == wmk.WMK_OK
     n = 3 * frames * tpf
     p = _last_attn(dry)
@@ -292,14 +292,14 @@ def test_moba_argument_errors(lib, dry):
                        (wmk.wmk_moba_desc(1560, 21, 3, 2), wmk.WMK_ERR_SHAPE),
                        (wmk.wmk_moba_desc(1560, 0, 3, 1), wmk.WMK_ERR_SHAPE),
                        (wmk.wmk_moba_desc(1 << 20, 1 << 12, 3, 1), wmk.WMK_ERR_SHAPE)]:
-        assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088, None, 0,
+        assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088,
                                       None) == status
     md = wmk.wmk_moba_desc(1560, 21, 3, 1)
-    assert lib.wmk_moba_attention(None, ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.1, None, 0, None) == \
+    assert lib.wmk_moba_attention(None, ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.1, None) == \
         wmk.WMK_ERR_NULL
-    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, 0, VBUF, OBUF, 0.1, None, 0, None) == \
+    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, 0, VBUF, OBUF, 0.1, None) == \
         wmk.WMK_ERR_NULL
-    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.0, None, 0, None) \
+    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.0, None) \
         == wmk.WMK_ERR_RANGE
 
 
@@ -503,6 +503,41 @@ def test_qk8_workspace_errors_and_plan(lib, dry):
     lib.wmk_cache_destroy(h)
 
 
+@pytest.mark.parametrize("S,W,cf,n_chunks", [(6, 8, 4, 5), (6, 8, 4, 6), (6, 8, 4, 3), (2, 5, 3, 6), (0, 7, 2, 9)])
+def test_qk8_spans_follow_time_order(lib, dry, S, W, cf, n_chunks):
+    """The FP8 call lists the resident frames oldest first (sinks, then the window), one
+    span per run of frames in adjacent slots, then the segments: the key sequence its
+    scale blocks are cut along.  The plain call on the same cache keeps slot order."""
+    tpf, H, D, L = 16, 2, 128, 2
+    d = _desc(L=L, H=H, D=D, tpf=tpf, S=S, W=W, cf=cf)
+    _, h = _init(lib, d)
+    for _ in range(n_chunks):
+        assert lib.wmk_cache_append_evict(h, 1, QBUF, SBUF, cf, None) == wmk.WMK_OK
+    F = n_chunks * cf
+    frame_b = tpf * H * D * 2
+    layer_b = (S + W) * frame_b
+    hd = wmk.wmk_head_desc(H, D, wmk.WMK_BF16)
+    slots = [oracle.slot_of_frame(f, S, W) for f in oracle.resident_frames(F, S, W)]
+    runs = []
+    for s_ in slots:
+        if runs and runs[-1][1] == s_:
+            runs[-1][1] = s_ + 1
+        else:
+            runs.append([s_, s_ + 1])
+    want, end = [], 0
+    for a, b in runs:
+        end += (b - a) * tpf
+        want.append((end, KBUF + layer_b + a * frame_b, VBUF + layer_b + a * frame_b))
+    want.append((end + 40, QBUF, SBUF))
+    assert _qk8(lib, h, hd, 40, [(QBUF, SBUF, 40)], 0x60000000, 1 << 30, layer=1) == wmk.WMK_OK
+    assert _spans(dry) == want
+    assert len(runs) <= 3 and (len(runs) == 1) == (slots == sorted(slots))
+    valid = oracle.valid_slots(F, S, W)
+    assert _attn(lib, h, 1, hd, 40, [(QBUF, SBUF, 40)]) == wmk.WMK_OK
+    assert _spans(dry) == [(valid * tpf, KBUF + layer_b, VBUF + layer_b), (valid * tpf + 40, QBUF, SBUF)]
+    lib.wmk_cache_destroy(h)
+
+
 def test_moba_train_and_backward_argument_errors(lib, dry):
     """Training forward (with log-sum-exp) and backward: argument checks before anything is
     planned; a valid backward logs its plan."""
@@ -540,3 +575,69 @@ def test_moba_train_and_backward_argument_errors(lib, dry):
     assert bwd() == wmk.WMK_OK
     last = dry.read_text().strip().splitlines()[-1]
     assert last == f"moba_bwd n={n} heads=12 part={21 * 1560} chunk={3 * 1560} parts=3"
+
+
+# ---- the Python binding's own argument checks (raised before any library call)
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(64, 2, 128, dtype=bf)
+    k = torch.zeros(100, 2, 128, dtype=bf)
+    bad = [
+        (lambda: wmk.chunk_attention(None, 0, q[:, :, :64]), "contiguous"),
+        (lambda: wmk.chunk_attention(None, 0, q, [(k, k[:99])]), "shape"),
+        (lambda: wmk.chunk_attention(None, 0, q, [(k.float(), k.float())]), "dtype"),
+        (lambda: wmk.chunk_attention(None, 0, q, [(k[:, :1].contiguous(), k[:, :1].contiguous())]), "shape"),
+        (lambda: wmk.chunk_attention(None, 0, q, out=torch.zeros(63, 2, 128, dtype=bf)), "shape"),
+        (lambda: wmk.chunk_attention(None, 0, q.view(64, 256)), "dimensions"),
+        (lambda: wmk.chunk_attention(None, 0, q, [(k, k)]), "device tensor"),
+        (lambda: wmk.moba_attention(q, q, q, tokens_per_frame=10, frames=2, chunk_frames=1), "MoBA sequence"),
+        (lambda: wmk.moba_attention(torch.zeros(60, 2, 128, dtype=bf), k, k, tokens_per_frame=10, frames=2,
+                                    chunk_frames=1), "shape"),
+        (lambda: wmk.moba_attention_train(torch.zeros(60, 2, 128, dtype=bf), torch.zeros(60, 2, 128, dtype=bf),
+                                          torch.zeros(60, 2, 128, dtype=bf), tokens_per_frame=10, frames=2,
+                                          chunk_frames=1, lse=torch.zeros(2, 59)), "shape"),
+        (lambda: wmk.cross_attention_train(q, k, k, chunk_q_tokens=32, env_tokens=10, local_tokens=40), "shape"),
+        (lambda: wmk.cross_attention_train(q, k, k, chunk_q_tokens=30, env_tokens=20, local_tokens=40), "chunks"),
+    ]
+    for fn, what in bad:
+        with pytest.raises(ValueError, match=what):
+            fn()
+
+
+def test_binding_scratch_is_per_stream(monkeypatch):
+    """The binding keeps one scratch buffer per (device, stream): two streams never share one."""
+    import torch
+    made = []
+
+    class FakeStream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    class FakeCtx:
+        def __init__(self, s):
+            pass
+
+        def __enter__(self):
+            return self
+
+        def __exit__(self, *a):
+            return False
+
+    real_empty = torch.empty
+
+    def fake_empty(n, dtype, device):
+        made.append(n)
+        return real_empty(n, dtype=dtype)
+
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda idx=None: FakeStream(11))
+    monkeypatch.setattr(torch.cuda, "stream", FakeCtx)
+    monkeypatch.setattr(torch, "empty", fake_empty)
+    monkeypatch.setattr(wmk, "_workspaces", {})
+    a = wmk.workspace("cuda:0", 100)
+    b = wmk.workspace("cuda:0", 100, FakeStream(22))
+    c = wmk.workspace("cuda:0", 50, FakeStream(11))
+    d = wmk.workspace("cuda:0", 200, FakeStream(22))
+    assert a is c and a is not b and d is not b and made == [100, 100, 200]

@@ -73,6 +73,33 @@ def test_moba_backward_small_all_elements(wmk, tpf, frames, cf, bidir, H):
     compare_grad(from_dev(gv), rv, "dv")
 
 
+def test_moba_backward_mid_size_all_elements(wmk):
+    """21 + 21 + 21 frames of 200 tokens in chunks of 3 (12 600 tokens, 2 heads): every
+    element of dq, dk and dv against the oracle.  A clean key of chunk 0 is read by the
+    clean rows of all 7 chunks and the noisy rows of chunks 1-6 (8 400 rows, 132 query
+    tiles), so the dK/dV kernel's long walks over query tiles are all compared."""
+    import torch
+    tpf, frames, cf, H, D = 200, 21, 3, 2, 128
+    n = 3 * frames * tpf
+    q, k, v, do = _inputs(n, H, D, seed=72)
+    say(f"moba bwd mid size n={n}")
+    tq, tk, tv, tdo = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    out, lse = wmk.moba_attention_train(tq, tk, tv, tokens_per_frame=tpf, frames=frames, chunk_frames=cf)
+    gq, gk, gv = wmk.moba_attention_backward(tq, tk, tv, out, tdo, lse, tokens_per_frame=tpf, frames=frames,
+                                             chunk_frames=cf)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(D)
+    say("  oracle backward")
+    rq, rk, rv = oracle.moba_attention_backward(q, k, v, do, tpf, frames, cf, 1, scale)
+    compare_grad(from_dev(gq), rq, "dq")
+    compare_grad(from_dev(gk), rk, "dk")
+    compare_grad(from_dev(gv), rv, "dv")
+    # the keys with the longest walks on their own: clean chunk 0
+    cl = cf * tpf
+    compare_grad(from_dev(gk)[:cl], rk[:cl], "dk of clean chunk 0")
+    compare_grad(from_dev(gv)[:cl], rv[:cl], "dv of clean chunk 0")
+
+
 def test_moba_backward_full_sequence(wmk):
     """21 + 21 + 21 frames of 1560 tokens, chunks of 3, 12 heads."""
     import torch

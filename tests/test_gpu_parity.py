@@ -232,6 +232,18 @@ def test_chunk_attention_832x464_18_slots(wmk):
         compare(outs[use_ws][rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"sampled rows ws={use_ws}")
     # split and unsplit schedules agree everywhere (different summation order only)
     compare(outs[True], as_f32(outs[False]), 4e-3, 2e-3, "split vs unsplit, all rows")
+    # every row of two heads against the oracle: head 0 (whole units only) and head 11, whose
+    # 256-row units run as the split tail (pieces plus the merge kernel) when the workspace is on
+    heads = [0, 11]
+    kc, vc = cm.logical_kv()
+    ka = np.ascontiguousarray(np.concatenate([kc, k])[:, heads])
+    va = np.ascontiguousarray(np.concatenate([vc, v])[:, heads])
+    nq, nk = cf * tpf, ka.shape[0]
+    assert nk == 18 * tpf
+    say(f"832x464: oracle on all {nq} rows of heads {heads}")
+    ref_h = oracle.attend(np.ascontiguousarray(q[:, heads]), ka, va, [[(0, nk)]] * nq, 1 / math.sqrt(D))
+    for use_ws in (False, True):
+        compare(outs[use_ws][:, heads], ref_h, BF16_MAX_ABS, BF16_REL_L2, f"all rows of heads {heads} ws={use_ws}")
     cache.close()
 
 

@@ -2,8 +2,9 @@
 the e4m3 codes and block scales of Q and K (read back from the workspace)
 bit for bit against the oracle's quantizer, the outputs against the oracle's
 quantized attention (bf16 bounds) on small ragged shapes and sampled rows at
-832x464 and 720p, and the quantization error against the exact attention (the looser
-bound of the quantized path)."""
+832x464 and 720p, the quantization error against the exact attention (the looser
+bound of the quantized path), and bit-identical outputs from two caches that hold
+the same frames with their rings wrapped at different slots."""
 import math
 
 import numpy as np
@@ -64,7 +65,7 @@ def _filled(wmk, S, W, cf, tpf, H, D, n_chunks, seed):
 
 
 def _check_codes(ws, cm, q, segments, H):
-    k_seq, _ = oracle.kernel_key_sequence(cm, segments)
+    k_seq, _ = oracle.qk8_key_sequence(cm, segments)
     k8, ks, q8, qs = _regions(ws, H, q.shape[0], k_seq.shape[0])
     kc, kss = oracle.quantize_e4m3_blocks(k_seq, 64)
     qc, qss = oracle.quantize_e4m3_blocks(q, 32)
@@ -138,7 +139,7 @@ def test_qk8_720p_sampled_heads(wmk):
     say("qk8 720p")
     out = wmk.chunk_attention_qk8(cache, 0, to_dev(q), [(to_dev(k), to_dev(v))], ws=ws)
     torch.cuda.synchronize()
-    k_seq, v_seq = oracle.kernel_key_sequence(cm, [(k, v)])
+    k_seq, v_seq = oracle.qk8_key_sequence(cm, [(k, v)])
     assert k_seq.shape[0] == nk
     k8, ks, q8, qs = _regions(ws, H, nq, nk)
     q32 = oracle.widen(q)[:, heads]
@@ -178,3 +179,42 @@ def test_qk8_default_workspace_repeats_bit_exactly(wmk):
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     cache.close()
+
+
+def test_qk8_same_frames_at_two_ring_phases_bit_identical(wmk):
+    """The 832x464 cache filled two ways so that it holds the same frame contents -- sinks
+    from chunks 0 and 1, the window from chunks 3 and 4 -- with the ring wrapped at different
+    slots (20 frames appended against 24): the FP8 scale blocks follow the time-ordered key
+    sequence, so the two calls quantize the same blocks and give bit-identical outputs,
+    which also equal the quantized oracle within the bf16 bounds."""
+    import torch
+    S, W, cf, tpf, H, D = 6, 8, 4, 1508, 12, 128
+    fin = [(host((cf * tpf, H, D), seed=48, chunk=c, step=4, kind=synth.KFIN),
+            host((cf * tpf, H, D), seed=48, chunk=c, step=4, kind=synth.VFIN)) for c in range(5)]
+    caches, models = [], []
+    for order in ((0, 1, 2, 3, 4), (0, 1, 2, 2, 3, 4)):
+        c = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=cf)
+        cm = oracle.CacheModel(S, W, tpf, H, D)
+        for i in order:
+            c.append_evict(0, to_dev(fin[i][0]), to_dev(fin[i][1]), cf)
+            cm.append(fin[i][0], fin[i][1], cf)
+        caches.append(c)
+        models.append(cm)
+    assert caches[0].slots(0)[0] != caches[1].slots(0)[0]
+    ka, _ = models[0].logical_kv()
+    kb, _ = models[1].logical_kv()
+    assert np.array_equal(ka, kb)
+    nq = cf * tpf
+    q, k, v = (host((nq, H, D), seed=49, kind=t) for t in (synth.Q, synth.K, synth.V))
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    say("qk8 two ring phases")
+    a = wmk.chunk_attention_qk8(caches[0], 0, tq, [(tk, tv)]).clone()
+    b = wmk.chunk_attention_qk8(caches[1], 0, tq, [(tk, tv)])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    rows = sample_rows(nq, np.random.default_rng(11), k=8, tile=256)
+    compare(from_dev(a)[rows], oracle.chunk_attention_qk8(models[0], q, [(k, v)], 1 / math.sqrt(D), rows=rows),
+            BF16_MAX_ABS, BF16_REL_L2, f"{len(rows)} rows vs quantized oracle")
+    for c in caches:
+        c.close()

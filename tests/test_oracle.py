@@ -741,18 +741,17 @@ def _lossless(shape, rows, seed):
 
 def test_qk8_is_exact_on_losslessly_quantizable_inputs():
     """Per-block power-of-two scales make quantization exact, so the quantized path equals the
-    plain attention; a wrong block partition (of Q rows, or of the kernel's key sequence)
+    plain attention; a wrong block partition (of Q rows, or of the time-ordered key sequence)
     would mix two blocks' scales and lose bits."""
     S, W, cf, tpf, H, D = 2, 3, 2, 24, 2, 64
     cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
     for c in range(5):                                   # ring wrapped: slot order != time order
         cm.append(_rand((cf * tpf, H, D), 200 + c), _rand((cf * tpf, H, D), 210 + c), cf)
-    k_seq, _ = oracle.kernel_key_sequence(cm, [])
-    nk = k_seq.shape[0]
-    kl = _lossless((nk + 40, H, D), 64, 3)               # the kernel-order keys, then a segment
-    valid = oracle.valid_slots(cm.F, S, W)
-    for s, f in enumerate(cm.slot_map()[:valid]):
-        cm.frames[f] = (kl[s * tpf:(s + 1) * tpf], cm.frames[f][1])
+    assert list(cm.slot_map()) != sorted(cm.slot_map())
+    nk = len(cm.resident()) * tpf
+    kl = _lossless((nk + 40, H, D), 64, 3)               # the keys in time order, then a segment
+    for i, f in enumerate(cm.resident()):
+        cm.frames[f] = (kl[i * tpf:(i + 1) * tpf], cm.frames[f][1])
     seg_k, seg_v = kl[nk:], _rand((40, H, D), 220)
     q = _lossless((70, H, D), 32, 4)
     a = oracle.chunk_attention_qk8(cm, q, [(seg_k, seg_v)], 0.05)
@@ -763,7 +762,7 @@ def test_qk8_is_exact_on_losslessly_quantizable_inputs():
     c = oracle.chunk_attention_qk8(cm, q, extra, 0.05)
     assert np.abs(c - oracle.chunk_attention(cm, q, extra, 0.05)).max() > 1e-9
     cm2_frames = dict(cm.frames)
-    f0 = cm.slot_map()[0]
+    f0 = cm.resident()[0]
     kk = cm.frames[f0][0].copy()
     kk[0, :, 0] *= 3.0                                   # one key 3x larger: its block's scale moves
     cm.frames[f0] = (kk, cm.frames[f0][1])
@@ -771,22 +770,57 @@ def test_qk8_is_exact_on_losslessly_quantizable_inputs():
     e = oracle.chunk_attention(cm, q, [(seg_k, seg_v)], 0.05)
     assert np.abs(d - e).max() > 1e-9
     cm.frames = cm2_frames
+    # the same lossless keys laid out in slot order instead (what a block cut along the
+    # ring's physical order would see) straddle the scale blocks differently: lossy
+    valid = oracle.valid_slots(cm.F, S, W)
+    for s_, f in enumerate(cm.slot_map()[:valid]):
+        cm.frames[f] = (kl[s_ * tpf:(s_ + 1) * tpf], cm.frames[f][1])
+    g = oracle.chunk_attention_qk8(cm, q, [(seg_k, seg_v)], 0.05)
+    assert np.abs(g - oracle.chunk_attention(cm, q, [(seg_k, seg_v)], 0.05)).max() > 1e-9
 
 
-def test_kernel_key_sequence_is_slot_order():
+def test_qk8_key_sequence_is_time_order():
+    """The FP8 key sequence lists the resident frames oldest first (sinks, then the window),
+    then the segments -- whatever slots the ring put them in."""
     S, W, cf, tpf, H, D = 2, 3, 2, 5, 1, 8
     cm = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    frames = {}
     for c in range(5):
-        cm.append(_rand((cf * tpf, H, D), 300 + c), _rand((cf * tpf, H, D), 310 + c), cf)
-    k, v = oracle.kernel_key_sequence(cm, [(np.ones((3, H, D), np.float32), np.zeros((3, H, D), np.float32))])
-    slots = cm.slot_map()
-    valid = oracle.valid_slots(cm.F, S, W)
-    assert k.shape[0] == valid * tpf + 3
-    for s in range(valid):
-        np.testing.assert_array_equal(k[s * tpf:(s + 1) * tpf], cm.frames[slots[s]][0])
-        np.testing.assert_array_equal(v[s * tpf:(s + 1) * tpf], cm.frames[slots[s]][1])
-    assert sorted(slots[:valid]) != list(slots[:valid])   # the ring has wrapped: not time order
+        k, v = _rand((cf * tpf, H, D), 300 + c), _rand((cf * tpf, H, D), 310 + c)
+        for j in range(cf):
+            frames[c * cf + j] = (k[j * tpf:(j + 1) * tpf], v[j * tpf:(j + 1) * tpf])
+        cm.append(k, v, cf)
+    k, v = oracle.qk8_key_sequence(cm, [(np.ones((3, H, D), np.float32), np.zeros((3, H, D), np.float32))])
+    # F = 10, S = 2, W = 3: sinks 0, 1 and the window 7, 8, 9 (slots 2 + (f - 2) % 3: 4, 2, 3)
+    want = [0, 1, 7, 8, 9]
+    assert [int(x) for x in cm.slot_map()] == [0, 1, 8, 9, 7]
+    assert k.shape[0] == len(want) * tpf + 3
+    for i, f in enumerate(want):
+        np.testing.assert_array_equal(k[i * tpf:(i + 1) * tpf], frames[f][0])
+        np.testing.assert_array_equal(v[i * tpf:(i + 1) * tpf], frames[f][1])
     np.testing.assert_array_equal(k[-3:], 1.0)
+
+
+def test_qk8_depends_on_resident_frames_not_ring_phase():
+    """Two caches holding the same frame contents, appended so that their rings wrap at
+    different slots, give bit-identical quantized attention."""
+    S, W, cf, tpf, H, D = 2, 4, 2, 40, 2, 64
+    chunks = [(_rand((cf * tpf, H, D), 500 + c), _rand((cf * tpf, H, D), 520 + c)) for c in range(5)]
+    a = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    b = oracle.CacheModel(S, W, tpf, H, D, dtype=np.float32)
+    for c in (0, 1, 2, 3):        # F = 8: sinks from chunk 0, window = chunks 2, 3
+        a.append(*chunks[c], cf)
+    for c in (0, 4, 4, 2, 3):     # F = 10: the same sinks and window, ring shifted by 2
+        b.append(*chunks[c], cf)
+    assert list(a.slot_map()) != list(b.slot_map())
+    ka, va = a.logical_kv()
+    kb, vb = b.logical_kv()
+    np.testing.assert_array_equal(ka, kb)
+    np.testing.assert_array_equal(va, vb)
+    q = _rand((50, H, D), 540)
+    seg = (_rand((30, H, D), 541), _rand((30, H, D), 542))
+    np.testing.assert_array_equal(oracle.chunk_attention_qk8(a, q, [seg], 0.1),
+                                  oracle.chunk_attention_qk8(b, q, [seg], 0.1))
 
 
 def test_dense_f64_attention_matches_c_core():
