@@ -44,13 +44,19 @@ def parse():
                     help="other workloads to run, comma separated: moba, moba_bwd, 720p, qk8, retained, rolling, "
                          "cross_train "
                          "(or all, none)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="query rows of the CPU oracle run (0: the whole call, all 6032 rows)")
     ap.add_argument("--occupancy-scan", action="store_true",
                     help="also time the attention kernel at 32, 256 and 2048 workgroups (12 heads' shape, "
                          "27136 keys): per-step time against occupancy (pair with a GRBM_GUI_ACTIVE counter pass "
                          "to read the shader clock)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--append-only", action="store_true",
+                    help="run only the rolling-session append/evict loop (30 layers, distinct sources and slots; "
+                         "for counter runs) and print its timing")
+    ap.add_argument("--skip-rates", action="store_true",
+                    help="skip the reference rates (MFMA microbenchmark, device-to-device copy)")
     return ap.parse_args()
 
 
@@ -75,6 +81,101 @@ def pmc_traffic():
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def rolling_appends(wmk, synth, torch, fill, stream, reps=4):
+    """Append/evict as the rolling session runs it: a 30-layer 832x464 cache (3.9 GB of
+    K and V) warmed to 14 resident frames, then one 4-frame append per layer from that
+    layer's own finalized chunk (30 distinct 37 MB sources, 1.1 GB), back to back.  The
+    working set (sources plus the slots written) is far above the 256 MB Infinity Cache,
+    so the bytes really move to and from HBM.  Returns microseconds per append."""
+    layers = 30
+    nq = CF * TPF
+    cache = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
+                      window_frames=W, chunk_frames=CF)
+    src = [(fill((nq, H, D), layer=l, step=4, kind=synth.KFIN), fill((nq, H, D), layer=l, step=4, kind=synth.VFIN))
+           for l in range(layers)]
+
+    def sweep():
+        for l in range(layers):
+            cache.append_evict(l, src[l][0], src[l][1], CF)
+
+    for _ in range(4):  # 16 frames appended: 14 resident, the ring has wrapped
+        sweep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        sweep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * layers)
+    del cache, src
+    torch.cuda.empty_cache()
+    return us, layers * reps
+
+
+def copy_calibration(torch, dev):
+    """Three plain device copies of 256 MiB (torch copy_ of contiguous bytes): a kernel of
+    known traffic (256 MiB read and 256 MiB written per launch) whose HBM byte counters
+    scale the counters of the kernels measured in the same run."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return 2 * n
+
+
+def reference_rates(torch, stream, append_bytes):
+    """Measured ceilings to read the roofline fractions against: the bf16 matrix-core rate
+    of a long stream of independent 32x32x16 MFMAs (clock under sustained load included),
+    and the device-to-device copy rate of hipMemcpyAsync (torch's copy_ of contiguous
+    bytes) on the append's pattern -- 30 layers x (K + V) of 18.5 MB each, all distinct,
+    beyond the Infinity Cache."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "kv_cache_attention_02_amd", "libwmk_rates.so"))
+    lib.wmk_rate_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.wmk_rate_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.wmk_rate_mfma_bf16_flops.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = cus * 8, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    assert lib.wmk_rate_mfma_bf16(blocks, iters, sink.data_ptr(), sp) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        lib.wmk_rate_mfma_bf16(blocks, iters, sink.data_ptr(), sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mfma_tflops = 3 * lib.wmk_rate_mfma_bf16_flops(blocks, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del sink
+    layers, each = 30, int(append_bytes // 4)
+    src = torch.empty(layers * 2 * each, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def copies():
+        for l in range(2 * layers):
+            dst[l * each:(l + 1) * each].copy_(src[l * each:(l + 1) * each])
+
+    copies()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        copies()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 3 * 2 * 2 * layers * each / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1),
+            "mfma_kernel": f"wmk_rate_mfma_bf16: {blocks} workgroups x 4 waves x {iters} x 4 independent "
+                           "v_mfma_f32_32x32x16_bf16",
+            "d2d_copy_GBps": round(copy_gbps, 1),
+            "d2d_copy": f"hipMemcpyAsync (torch copy_) of {2 * layers} distinct {each / 1e6:.1f} MB ranges"}
 
 
 def main():
@@ -105,6 +206,16 @@ def main():
     kv_tokens = (S + W + CF) * TPF
     flops = 4.0 * D * H * nq * kv_tokens                 # allowed pairs x 4 * head_dim
     append_bytes = 2.0 * 2 * nq * H * D * 2              # K + V chunk, read + write
+
+    if args.append_only:
+        us, n = rolling_appends(wmk, synth, torch, fill, stream, reps=args.steps)
+        res = {"append_evict_rolling_us": round(us, 2), "appends": n,
+               "GBps": round(append_bytes / (us * 1e-6) / 1e9, 1),
+               "frac_hbm": round(append_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        if args.copy_calibration:
+            res["copy_calibration_bytes"] = copy_calibration(torch, dev)
+        print(json.dumps(res))
+        return
 
     # ---- resident inputs: a cache warmed to 14 frames plus a pool of finalized chunks
     cache = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
@@ -146,8 +257,11 @@ def main():
     slots, F = cache.slots(0)
     assert sum(s >= 0 for s in slots) == S + W, slots
 
-    # append/evict kernel throughput: back-to-back launches between one event
-    # pair (the per-step brackets above also hold the dispatch gap)
+    # append/evict kernel throughput in the rolling session's pattern (30 layers,
+    # distinct sources and destinations: real HBM traffic), and back to back on
+    # this one-layer cache (4 pooled sources: a working set that fits in the
+    # Infinity Cache) for comparison
+    roll_us, roll_n = rolling_appends(wmk, synth, torch, fill, stream)
     n_app = 50
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record(stream)
@@ -191,23 +305,26 @@ def main():
         "append_evict": {
             "kernel": "copy_ranges_kernel",
             "bytes_per_launch": append_bytes,
-            "us_back_to_back": round(append_b2b_us, 2),
-            "GBps": round(append_bytes / (append_b2b_us * 1e-6) / 1e9, 1),
-            "frac_hbm": round(append_bytes / (append_b2b_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "workload": f"rolling session: {roll_n} appends over 30 layers of a 3.9 GB cache, each from its own "
+                        "37 MB source (working set beyond the Infinity Cache)",
+            "us_avg": round(roll_us, 2),
+            "GBps": round(append_bytes / (roll_us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(append_bytes / (roll_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "us_one_layer_4_sources_in_cache": round(append_b2b_us, 2),
             "us_in_step_avg": round(float(append_ms.mean()) * 1e3, 2),
             "us_in_step_median": round(float(np.median(append_ms)) * 1e3, 2),
         },
         "ms_per_chunk_step_attention_only": round(attn_avg, 4),
     }
 
+    if not args.skip_rates:
+        rates = reference_rates(torch, stream, append_bytes)
+        rates["attention_frac_of_mfma_rate"] = round(result["roofline"]["achieved"] / rates["mfma_bf16_tflops"], 4)
+        rates["append_frac_of_d2d_copy"] = round(result["append_evict"]["GBps"] / rates["d2d_copy_GBps"], 4)
+        result["reference_rates"] = rates
+
     if args.copy_calibration:
-        n = 256 << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = 2 * n
+        result["copy_calibration_bytes"] = copy_calibration(torch, dev)
 
     if args.occupancy_scan:
         result["occupancy_scan"] = occupancy_scan(wmk, synth, torch, fill)
@@ -438,14 +555,17 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps, which):
 
 
 def cpu_baseline(args, flops, nq, kv_tokens):
-    """The oracle (fp64 C, OpenMP, as it stands) on a bounded sample of the same
-    workload: a few query rows of the 832x464 step against all 27144 keys."""
+    """The oracle (fp64 C, OpenMP, as it stands) on the same workload: one whole 832x464
+    chunk-attention call -- all 6032 query rows x 12 heads against all 27144 keys -- on
+    every host thread OpenMP is given, plus a one-thread run of a row sample for context."""
+    import ctypes
+
     import numpy as np
 
     import oracle
     import synth
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     cm = oracle.CacheModel(S, W, TPF, H, D)
     for c in range(4):
         kf = synth.normal(nq * H * D, seed=args.seed, chunk=c, step=4, kind=synth.KFIN).reshape(nq, H, D)
@@ -454,32 +574,50 @@ def cpu_baseline(args, flops, nq, kv_tokens):
     qh = synth.normal(nq * H * D, seed=args.seed, chunk=4, kind=synth.Q).reshape(nq, H, D)
     kh = synth.normal(nq * H * D, seed=args.seed, chunk=4, kind=synth.K).reshape(nq, H, D)
     vh = synth.normal(nq * H * D, seed=args.seed, chunk=4, kind=synth.V).reshape(nq, H, D)
-    oracle.chunk_attention(cm, qh, [(kh, vh)], 1 / math.sqrt(D), rows=np.arange(8))   # warm-up
-    rows = np.arange(64)
+    scale = 1 / math.sqrt(D)
+    rows = np.arange(nq) if args.cpu_rows <= 0 else np.linspace(0, nq - 1, args.cpu_rows).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.chunk_attention(cm, qh, [(kh, vh)], 1 / math.sqrt(D), rows=rows)
+    oracle.chunk_attention(cm, qh, [(kh, vh)], scale, rows=rows)
     dt = time.perf_counter() - t0
-    n = int(min(nq, max(64, 64 * args.cpu_seconds / max(dt, 1e-3))))
-    rows = np.linspace(0, nq - 1, n).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.chunk_attention(cm, qh, [(kh, vh)], 1 / math.sqrt(D), rows=rows)
-    dt = time.perf_counter() - t0
-    sample_flops = flops * n / nq
-    return {"value": round(sample_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {nq} query rows x {H} heads of the 832x464 step against all {kv_tokens} keys "
-                      f"({dt:.1f} s, fp64)",
-            "ms_per_chunk_step_extrapolated": round(dt * 1e3 * nq / n, 1),
-            "cpu_model": _cpu_model()}
+    res = {"value": round(flops * len(rows) / nq / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle",
+           "sample": (f"one whole 832x464 call: all {nq} query rows x {H} heads against all {kv_tokens} keys "
+                      if len(rows) == nq else f"{len(rows)} of {nq} query rows x {H} heads against all {kv_tokens} "
+                                              "keys of the 832x464 call ") + f"({dt:.1f} s, fp64, {threads} threads)",
+           "ms_per_chunk_step": round(dt * 1e3 * nq / len(rows), 1),
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    # one thread, on a row sample (the whole call would take minutes)
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        sample = np.linspace(0, nq - 1, 48).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.chunk_attention(cm, qh, [(kh, vh)], scale, rows=sample)
+        dt1 = time.perf_counter() - t0
+        gomp.omp_set_num_threads(threads)
+        res["one_thread"] = {"value": round(flops * len(sample) / nq / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                             "sample": f"{len(sample)} of {nq} query rows ({dt1:.1f} s)",
+                             "ms_per_chunk_step_extrapolated": round(dt1 * 1e3 * nq / len(sample), 1)}
+    except OSError:
+        pass
+    return res
 
 
 def _cpu_model():
+    """The host CPU: model name plus family / model / stepping numbers from /proc/cpuinfo."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "vendor_id", "cpu family", "model", "stepping") and k not in info:
+                    info[k] = v
+            if not line.strip() and info:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{info.get('model name', 'unknown')} ({info.get('vendor_id', '?')}, family {info.get('cpu family', '?')}"
+            f" model {info.get('model', '?')} stepping {info.get('stepping', '?')})")
 
 
 if __name__ == "__main__":

@@ -7,6 +7,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["wmk_api.cpp", "attn_bf16.hip", "attn_f32.hip", "cache_append.hip", "quant_fp8.hip", "attn_bwd.hip"]
 LIB = os.path.join(PKG, "libwmk.so")
+# measurement-only kernels (reference rates of the benchmark), kept out of libwmk.so
+RATES_SOURCE = "rates.hip"
+RATES_LIB = os.path.join(PKG, "libwmk_rates.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
@@ -36,6 +39,12 @@ def build(verbose=False, extra_flags=()):
     os.replace(LIB + ".tmp", LIB)
     for o in objs:
         os.remove(o)
+    cmd = [HIPCC] + FLAGS + list(extra_flags) + ["-x", "hip", os.path.join(CSRC, RATES_SOURCE), "-o",
+                                                  RATES_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(RATES_LIB + ".tmp", RATES_LIB)
     return LIB
 
 
