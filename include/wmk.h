@@ -188,6 +188,25 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
                                int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out, float scale,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* wmk_chunk_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and the same split-tail plan as
+ * wmk_chunk_attention given an ample workspace, but the split tail's scratch
+ * is a device array the library holds -- one per GPU, 34,078,720 bytes, kept
+ * until the process ends -- and the call allocates nothing.  Its address is
+ * looked up on the first call on each device.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, or other
+ * threads without ordering) race and must not be issued.  Nothing in the
+ * array needs clearing between calls.  Arguments, layout and ownership as
+ * for wmk_chunk_attention.
+ * Errors: as wmk_chunk_attention; a split tail needing more than the array
+ * (more than 256 pieces: a device with more than 256 resident attention
+ * workgroups) -> WMK_ERR_CAPACITY; the array's address not available ->
+ * WMK_ERR_HIP.  Nothing is enqueued on error. */
+wmk_status wmk_chunk_attention_noalloc(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
+                                       int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out,
+                                       float scale, hipStream_t stream);
+
 /* Workspace bytes for wmk_chunk_attention_qk8 with q_tokens queries and up to
  * kv_tokens keys (cache part plus segments): the FP8 codes and scales of Q and
  * K, plus the optional split-tail scratch of wmk_attention_workspace_bytes.

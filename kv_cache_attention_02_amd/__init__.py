@@ -61,6 +61,9 @@ _SIGNATURES = {
     "wmk_chunk_attention": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
                                            ctypes.POINTER(wmk_kv_segment), ctypes.c_int32, _P, ctypes.c_float, _P,
                                            ctypes.c_size_t, _P]),
+    "wmk_chunk_attention_noalloc": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P,
+                                                   ctypes.c_int32, ctypes.POINTER(wmk_kv_segment), ctypes.c_int32,
+                                                   _P, ctypes.c_float, _P]),
     "wmk_attention_qk8_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_head_desc), ctypes.c_int32,
                                                             ctypes.c_int64]),
     "wmk_chunk_attention_qk8": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(wmk_head_desc), _P, ctypes.c_int32,
@@ -318,6 +321,23 @@ def chunk_attention(cache, layer, q, segments=(), out=None, scale=None, use_work
         _check(load().wmk_chunk_attention_retained(cache.handle if cache is not None else None, layer, arr,
                                                    len(keep), ctypes.byref(hd), _ptr(q), nq, segs, len(segments),
                                                    _ptr(out), scale, ws, wsb, _stream_ptr(stream)))
+    return out
+
+
+def chunk_attention_noalloc(cache, layer, q, out, segments=(), scale=None, stream=None):
+    """chunk_attention through wmk_chunk_attention_noalloc: the split tail's scratch is the
+    library's own device array, so nothing is allocated (``out`` is required)."""
+    _check_tensor("q", q)
+    nq, H, D = q.shape
+    _check_cache(cache, q)
+    _check_like("out", out, q)
+    hd = wmk_head_desc(H, D, _dtype_code(q.dtype))
+    segs = _segments(segments, q)
+    _on_device(q=q)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(load().wmk_chunk_attention_noalloc(cache.handle if cache is not None else None, layer, ctypes.byref(hd),
+                                              _ptr(q), nq, segs, len(segments), _ptr(out), scale,
+                                              _stream_ptr(stream)))
     return out
 
 

@@ -5,7 +5,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["wmk_api.cpp", "attn_bf16.hip", "attn_f32.hip", "cache_append.hip", "quant_fp8.hip", "attn_bwd.hip"]
+SOURCES = ["wmk_api.cpp", "attn_bf16.hip", "attn_f32.hip", "cache_append.hip", "quant_fp8.hip", "attn_bwd.hip",
+           "noalloc.hip"]
 LIB = os.path.join(PKG, "libwmk.so")
 # measurement-only kernels (reference rates of the benchmark), kept out of libwmk.so
 RATES_SOURCE = "rates.hip"

@@ -157,24 +157,27 @@ constexpr int kBK = 64;
 constexpr int kMinTilesPerPiece = 8;
 
 // Split the last, partly filled round of units over the whole GPU when the
-// caller gave enough workspace.
-void plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws, size_t ws_bytes) {
+// caller gave enough workspace.  Returns the workspace bytes that split needs
+// (0 when the call gets no split whatever the workspace).
+size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws, size_t ws_bytes) {
     p.split_units = 0;
     p.splits = 1;
     p.ws = nullptr;
-    // (the pieces store 16-byte vectors: a misaligned workspace is not used)
-    if (ws == nullptr || ((uintptr_t)ws & 15) != 0 || tiles_per_unit < 2 * kMinTilesPerPiece) return;
+    if (tiles_per_unit < 2 * kMinTilesPerPiece) return 0;
     const DeviceInfo di = device_info();
     const int slots = di.cus * (head_dim == 64 ? di.bpc64 : di.bpc128);
-    if (slots <= 0) return;
+    if (slots <= 0) return 0;
     const int32_t rounds = p.n_units / slots, tail = p.n_units % slots;
-    if (rounds < 1 || tail == 0) return;
+    if (rounds < 1 || tail == 0) return 0;
     int32_t splits = std::min<int32_t>(slots / tail, tiles_per_unit / kMinTilesPerPiece);
-    if (splits < 2) return;
-    if (wmk::attn_bf16_split_ws_bytes(head_dim, tail, splits) > ws_bytes) return;
+    if (splits < 2) return 0;
+    const size_t need = wmk::attn_bf16_split_ws_bytes(head_dim, tail, splits);
+    // (the pieces store 16-byte vectors: a misaligned workspace is not used)
+    if (ws == nullptr || ((uintptr_t)ws & 15) != 0 || need > ws_bytes) return need;
     p.split_units = tail;
     p.splits = splits;
     p.ws = ws;
+    return need;
 }
 
 // Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
@@ -243,8 +246,11 @@ struct Qk8Bufs {
     float* q8_scale;
 };
 
+// strict_ws: the workspace is the library's own fixed scratch; a split that
+// does not fit is an error rather than a reason to run unsplit, so the call
+// plans exactly as wmk_chunk_attention with an ample workspace would.
 wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, size_t ws_bytes,
-                         hipStream_t stream, const Qk8Bufs* qk8 = nullptr) {
+                         hipStream_t stream, const Qk8Bufs* qk8 = nullptr, bool strict_ws = false) {
     if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
     hipError_t e;
     if (dtype == WMK_F32) {
@@ -272,7 +278,10 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
             if (call.mask.mode == wmk::kMaskCross)
                 tiles = (call.mask.env_len + kBK - 1) / kBK + (call.mask.chunk_len + kBK - 1) / kBK;
             p.xcd_remap = 1;
-            plan_split(p, call.head_dim, tiles, ws, ws_bytes);
+            const size_t need = plan_split(p, call.head_dim, tiles, ws, ws_bytes);
+            if (strict_ws && need > ws_bytes)
+                return fail(WMK_ERR_CAPACITY, "the split tail of this call needs %zu bytes of scratch; the library "
+                            "holds %zu", need, ws_bytes);
         }
         if (qk8 != nullptr) {
             p.k8 = qk8->k8;
@@ -347,7 +356,7 @@ size_t qk8_bytes(int32_t heads, int32_t q_tokens, int64_t kv_tokens, Qk8Bufs* b,
 wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t* keep, int32_t n_keep,
                                 const wmk_head_desc* hd, const void* q, int32_t q_tokens, const wmk_kv_segment* seg,
                                 int32_t n_seg, void* out, float scale, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream, bool qk8 = false) {
+                                hipStream_t stream, bool qk8 = false, bool strict_ws = false) {
     wmk_status s = check_head(hd);
     if (s != WMK_OK) return s;
     if (qk8 && hd->dtype != WMK_BF16) return fail(WMK_ERR_DTYPE, "FP8 QK^T takes bf16 inputs");
@@ -436,7 +445,7 @@ wmk_status chunk_attention_impl(const wmk_cache* c, int32_t layer, const int64_t
     call.kv_total = (int32_t)total;
     call.scale = scale;
     call.mask.mode = wmk::kMaskNone;
-    if (!qk8) return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
+    if (!qk8) return run_attention(call, hd->dtype, workspace, workspace_bytes, stream, nullptr, strict_ws);
     Qk8Bufs bufs;
     const size_t need = qk8_bytes(hd->num_heads, q_tokens, total, &bufs, (char*)workspace);
     if (workspace == nullptr || workspace_bytes < need)
@@ -612,6 +621,20 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return chunk_attention_impl(c, layer, nullptr, 0, hd, q, q_tokens, seg, n_seg, out, scale, workspace,
                                 workspace_bytes, stream);
+}
+
+wmk_status wmk_chunk_attention_noalloc(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
+                                       int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out,
+                                       float scale, hipStream_t stream) {
+    void* ws = nullptr;
+    if (dry_run_path() != nullptr) {
+        ws = (void*)(uintptr_t)0x7000000000ull;  // no device: a stand-in address, only planned with
+    } else {
+        const hipError_t e = wmk::noalloc_scratch(&ws);
+        if (e != hipSuccess) return fail(WMK_ERR_HIP, "library scratch not available: %s", hipGetErrorString(e));
+    }
+    return chunk_attention_impl(c, layer, nullptr, 0, hd, q, q_tokens, seg, n_seg, out, scale, ws,
+                                wmk::noalloc_scratch_bytes(), stream, false, true);
 }
 
 size_t wmk_attention_qk8_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens, int64_t kv_tokens) {

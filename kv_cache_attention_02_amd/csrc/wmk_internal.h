@@ -126,6 +126,12 @@ struct MobaBwd {
 };
 hipError_t launch_moba_backward(const MobaBwd& b, hipStream_t s);
 
+// Library-held split-tail scratch of wmk_chunk_attention_noalloc: its size,
+// and the device address of the current device's copy (looked up on the
+// first call on each device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 // fp32 attention (plain SIMT; correctness path for fp32 inputs).
 hipError_t launch_attn_f32(const AttnCall& c, hipStream_t s);
 

@@ -641,3 +641,32 @@ def test_binding_scratch_is_per_stream(monkeypatch):
     c = wmk.workspace("cuda:0", 50, FakeStream(11))
     d = wmk.workspace("cuda:0", 200, FakeStream(22))
     assert a is c and a is not b and d is not b and made == [100, 100, 200]
+
+
+def test_noalloc_plans_like_the_workspace_entry(lib, dry):
+    """wmk_chunk_attention_noalloc plans exactly as wmk_chunk_attention with an ample
+    workspace (same split units and pieces), its scratch at the library's own address,
+    and refuses bad arguments before planning anything."""
+    d = _desc()
+    _, h = _init(lib, d)
+    for _ in range(4):
+        assert lib.wmk_cache_append_evict(h, 0, QBUF, SBUF, 4, None) == wmk.WMK_OK
+    hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
+    for nq, nk in ((6032, 6032), (5500, 3016), (700, 100)):
+        seg = (wmk.wmk_kv_segment * 1)(wmk.wmk_kv_segment(QBUF, SBUF, nk))
+        assert lib.wmk_chunk_attention_noalloc(h, 0, ctypes.byref(hd), QBUF, nq, seg, 1, OBUF, 0.088,
+                                               None) == wmk.WMK_OK
+        a = _last_attn(dry)
+        assert _attn(lib, h, 0, hd, nq, [(QBUF, SBUF, nk)], ws=0x60000000, wsb=1 << 30) == wmk.WMK_OK
+        b = _last_attn(dry)
+        assert a == b, (nq, a, b)
+    assert (a["split_units"], a["splits"]) == ("0", "1")
+    seg = (wmk.wmk_kv_segment * 1)(wmk.wmk_kv_segment(QBUF, SBUF, 6032))
+    n_before = len(dry.read_text().splitlines())
+    for args, status in [((h, 0, ctypes.byref(hd), QBUF, 6032, seg, 1, OBUF, 0.0), wmk.WMK_ERR_RANGE),
+                         ((h, 1, ctypes.byref(hd), QBUF, 6032, seg, 1, OBUF, 0.088), wmk.WMK_ERR_RANGE),
+                         ((h, 0, None, QBUF, 6032, seg, 1, OBUF, 0.088), wmk.WMK_ERR_NULL),
+                         ((h, 0, ctypes.byref(hd), QBUF + 4, 6032, seg, 1, OBUF, 0.088), wmk.WMK_ERR_ALIGN)]:
+        assert lib.wmk_chunk_attention_noalloc(*args, None) == status
+    assert len(dry.read_text().splitlines()) == n_before
+    lib.wmk_cache_destroy(h)
