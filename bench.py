@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--append-only", action="store_true",
                     help="run only the rolling-session append/evict loop (30 layers, distinct sources and slots; "
                          "for counter runs) and print its timing")
+    ap.add_argument("--step-profile", action="store_true",
+                    help="run the 832x464 call on the step-profile build of the library (libwmk_stepprof.so: "
+                         "per-wave shader cycles of each phase of a 64-key step) and print the per-step budget")
     ap.add_argument("--skip-rates", action="store_true",
                     help="skip the reference rates (MFMA microbenchmark, device-to-device copy)")
     return ap.parse_args()
@@ -113,6 +116,57 @@ def rolling_appends(wmk, synth, torch, fill, stream, reps=4):
     del cache, src
     torch.cuda.empty_cache()
     return us, layers * reps
+
+
+def step_profile(wmk, synth, torch, np, fill, stream, flops):
+    """The 832x464 call on the step-profile build: per wave, the shader cycles of each phase
+    of its 64-key steps -- [A] (S^T of the next tile on the matrix core beside this tile's
+    second-half weights), [B] (P V beside the next tile's row max and first-half weights),
+    the wait for the step's own direct loads, the barrier, and the issue code before [A] --
+    averaged per step, over the 256 full units and over the split tail's pieces; waves
+    0-3 and 4-7 (the two waves of each SIMD) separately; and the shader clock from the
+    same span on the 100 MHz real-time counter."""
+    import ctypes
+    nq = CF * TPF
+    cache = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S, window_frames=W,
+                      chunk_frames=CF)
+    for c in range(4):
+        cache.append_evict(0, fill((nq, H, D), chunk=c, step=4, kind=synth.KFIN),
+                           fill((nq, H, D), chunk=c, step=4, kind=synth.VFIN), CF)
+    q, k, v = (fill((nq, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
+    out = torch.empty_like(q)
+    for _ in range(5):
+        wmk.chunk_attention(cache, 0, q, [(k, v)], out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    wmk.chunk_attention(cache, 0, q, [(k, v)], out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lib = wmk.load()
+    lib.wmk_step_profile_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    buf = np.zeros((4096 * 8, 9), np.uint64)
+    assert lib.wmk_step_profile_read(buf.ctypes.data, buf.nbytes) == 0
+    wg = buf[:512 * 8].astype(np.float64).reshape(512, 8, 9)
+    names = ["A_qk_next_and_weights", "B_pv_and_next_max_weights", "wait_own_loads", "barrier", "issue_before_A"]
+    res = {"library": "libwmk_stepprof.so", "call_ms": round(e0.elapsed_time(e1), 4),
+           "call_tflops": round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)}
+    for label, sl in (("full_units", slice(0, 256)), ("split_pieces", slice(256, 512))):
+        x = wg[sl]
+        part = {}
+        for waves, tag in ((slice(0, 8), "all_waves"), (slice(0, 4), "waves_0_3"), (slice(4, 8), "waves_4_7")):
+            y = x[:, waves].reshape(-1, 9)
+            y = y[y[:, 5] > 0]
+            per = {nm: round(float(np.mean(y[:, i] / y[:, 5])), 1) for i, nm in enumerate(names)}
+            per["phases_sum"] = round(sum(per.values()), 1)
+            per["cycles_per_step_span"] = round(float(np.mean(y[:, 6] / y[:, 5])), 1)
+            if tag == "all_waves":
+                per["steps_per_wave"] = round(float(np.mean(y[:, 5])), 1)
+                per["shader_clock_GHz"] = round(float(np.mean(y[:, 6] / (y[:, 8] * 10.0))), 3)
+            part[tag] = per
+        res[label] = part
+    del cache
+    return res
 
 
 def copy_calibration(torch, dev):
@@ -191,6 +245,9 @@ def main():
     import kv_cache_attention_02_amd as wmk
     import synth
 
+    if args.step_profile:
+        wmk.LIB_PATH = os.path.join(ROOT, "kv_cache_attention_02_amd", "libwmk_stepprof.so")
+
     assert torch.cuda.is_available(), "bench.py needs an MI355X"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -206,6 +263,10 @@ def main():
     kv_tokens = (S + W + CF) * TPF
     flops = 4.0 * D * H * nq * kv_tokens                 # allowed pairs x 4 * head_dim
     append_bytes = 2.0 * 2 * nq * H * D * 2              # K + V chunk, read + write
+
+    if args.step_profile:
+        print(json.dumps(step_profile(wmk, synth, torch, np, fill, stream, flops)))
+        return
 
     if args.append_only:
         us, n = rolling_appends(wmk, synth, torch, fill, stream, reps=args.steps)

@@ -61,6 +61,26 @@
 #include "wmk_internal.h"
 
 namespace wmk {
+
+#ifdef WMK_STEP_PROFILE
+// Step profile (a separate build, libwmk_stepprof.so): per wave, the shader
+// cycles (s_memtime) spent in each phase of the key-tile steps, summed over the
+// launch -- [A], [B], the wait for the step's own direct loads, the barrier and
+// the issue code before [A] -- plus the step count, the span from the first
+// step's start to the last step's end, the unit, and that span on the 100 MHz
+// real-time counter (s_memrealtime), which gives the shader clock.  Read back with
+// wmk_step_profile_read after the launch.  Each timestamp is a scalar memory
+// read the following code waits on, so the profiled kernel runs a few percent
+// slower than the product build.
+__device__ unsigned long long g_step_prof[4096 * 8][9];
+extern "C" __attribute__((visibility("default"))) int wmk_step_profile_read(void* host, size_t bytes) {
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_step_prof), bytes, 0, hipMemcpyDeviceToHost);
+}
+#define WMK_STAMP(x) x = __builtin_amdgcn_s_memtime()
+#else
+#define WMK_STAMP(x) (void)0
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -673,7 +693,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     // One key tile; ST (compile time) is the buffer holding K(it) and V(it);
     // K(it+1) is in the other K buffer.  Fills K(it+2) into K buffer ST and
     // V(it+1) into the other V buffer while it computes.  LAST: no next tile.
+    [[maybe_unused]] uint64_t prof[7] = {};  // step profile: A, B, load wait, barrier, issue, steps, span
+    [[maybe_unused]] uint64_t prof_first = 0, real_first = 0, real_last = 0;
     auto step = [&](auto st_tag, auto last_tag, int32_t it) __attribute__((always_inline)) {
+        [[maybe_unused]] uint64_t pc_s = 0, pc0 = 0, pc1 = 0, pc2 = 0, pc3 = 0, pc4 = 0;
+        WMK_STAMP(pc_s);
         constexpr int ST = decltype(st_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
         const Buf<D>& kcur = ST ? kb1 : kb0;
@@ -719,6 +743,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         }
 
         if (wave_has_rows) {
+            WMK_STAMP(pc0);
             // Wave priority falls as the step progresses (3 at the start, 2 and 1
             // within [A], 0 halfway through [B]): of the two waves of a SIMD the one
             // behind keeps the higher priority, so both reach the barrier together.
@@ -812,6 +837,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             // below, and would otherwise be sunk past it
             asm volatile("" ::"v"(pf1[0]), "v"(pf1[1]), "v"(lsum));
             l_run += lsum;
+            WMK_STAMP(pc1);
 
             // [B] O^T += V(it)^T P(it)^T on the matrix core (V^T fragments VPF
             //     MFMAs ahead), next to the row max of S^T(it+1), the new
@@ -896,9 +922,28 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
                 pf0[0] = pn0[0];
                 pf0[1] = pn0[1];
             }
+            WMK_STAMP(pc2);
         }
         __builtin_amdgcn_s_waitcnt(0);
+        WMK_STAMP(pc3);
         __syncthreads();
+        WMK_STAMP(pc4);
+#ifdef WMK_STEP_PROFILE
+        if (wave_has_rows) {
+            prof[0] += pc1 - pc0;
+            prof[1] += pc2 - pc1;
+            prof[2] += pc3 - pc2;
+            prof[3] += pc4 - pc3;
+            prof[4] += pc0 - pc_s;
+            prof[5] += 1;
+            if (prof_first == 0) {
+                prof_first = pc_s;
+                real_first = __builtin_amdgcn_s_memrealtime();
+            }
+            prof[6] = pc4 - prof_first;
+            if (LAST) real_last = __builtin_amdgcn_s_memrealtime();
+        }
+#endif
         if constexpr (Q8 && !LAST) {
             cs_a = cs_b;
             cs_b = cs0 * (sk_next > 0.0f ? sk_next : 1.0f);
@@ -917,6 +962,14 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         step(I0{}, Last{}, it);
     }
 
+#ifdef WMK_STEP_PROFILE
+    if (lane == 0 && blockIdx.x < 4096) {
+        unsigned long long* e = g_step_prof[blockIdx.x * NW + wave];
+        for (int i = 0; i < 7; ++i) e[i] = prof[i];
+        e[7] = (unsigned long long)head << 32 | (unsigned long long)qt << 8 | (unsigned long long)(piece < 0 ? 255 : piece);
+        e[8] = real_last - real_first;
+    }
+#endif
     const float l_tot = pair_sum(l_run);
     __bf16* op = (__bf16*)c.out + (int64_t)row * stride + (int64_t)head * D;
 
