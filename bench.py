@@ -224,12 +224,29 @@ def reference_rates(torch, stream, append_bytes):
     torch.cuda.synchronize()
     copy_gbps = 3 * 2 * 2 * layers * each / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
+    # fp32 atomic adds (no return) in the dQ-accumulation pattern of a fused backward:
+    # 32 KiB blocks (64 rows x 128 dims, row stride 12 heads) at random 64-row tiles
+    lib.wmk_rate_atomic_add_f32.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p]
+    n_tiles, heads, ablocks, rounds = 1536, 12, 4608, 32
+    acc = torch.zeros(n_tiles * 64 * heads * 128, dtype=torch.float32, device="cuda")
+    assert lib.wmk_rate_atomic_add_f32(acc.data_ptr(), n_tiles, heads, ablocks, rounds, sp) == 0
+    torch.cuda.synchronize()
+    e0.record(stream)
+    lib.wmk_rate_atomic_add_f32(acc.data_ptr(), n_tiles, heads, ablocks, rounds, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    atomic_gbps = ablocks * rounds * 64 * 128 * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del acc
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": round(mfma_tflops, 1),
             "mfma_kernel": f"wmk_rate_mfma_bf16: {blocks} workgroups x 4 waves x {iters} x 4 independent "
                            "v_mfma_f32_32x32x16_bf16",
             "d2d_copy_GBps": round(copy_gbps, 1),
-            "d2d_copy": f"hipMemcpyAsync (torch copy_) of {2 * layers} distinct {each / 1e6:.1f} MB ranges"}
+            "d2d_copy": f"hipMemcpyAsync (torch copy_) of {2 * layers} distinct {each / 1e6:.1f} MB ranges",
+            "atomic_add_f32_GBps": round(atomic_gbps, 1),
+            "atomic_add": f"wmk_rate_atomic_add_f32: {ablocks} x {rounds} blocks of 64 x 128 fp32 added at random "
+                          f"64-row tiles of a [{n_tiles * 64}][{heads}][128] buffer"}
 
 
 def main():
@@ -563,34 +580,46 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps, which):
         rc = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
                        window_frames=W, chunk_frames=CF)
         pool = [tuple(fill((nq, H, D), chunk=i, kind=t) for t in (synth.Q, synth.K, synth.V)) for i in range(2)]
-        fin = [tuple(fill((nq, H, D), chunk=i, step=4, kind=t) for t in (synth.KFIN, synth.VFIN)) for i in range(2)]
+        # each layer appends its own finalized chunk (30 distinct sources, as in a real session)
+        fin = [tuple(fill((nq, H, D), layer=l, step=4, kind=t) for t in (synth.KFIN, synth.VFIN)) for l in range(layers)]
         ro = torch.empty((nq, H, D), dtype=torch.bfloat16, device=dev)
 
-        def chunk(ci):
+        app_ev = []
+
+        def chunk(ci, ev=False):
             for st in range(steps):
                 for l in range(layers):
                     rq, rk, rv = pool[(st + l) % 2]
                     wmk.chunk_attention(rc, l, rq, [(rk, rv)], out=ro)
+            if ev:
+                app_ev.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                app_ev[-1][0].record(stream)
             for l in range(layers):
-                rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
+                rc.append_evict(l, fin[l][0], fin[l][1], CF)
+            if ev:
+                app_ev[-1][1].record(stream)
 
         for ci in range(4):  # warm the cache to 14 resident frames
             for l in range(layers):
-                rc.append_evict(l, fin[ci % 2][0], fin[ci % 2][1], CF)
+                rc.append_evict(l, fin[l][0], fin[l][1], CF)
         chunk(4)
         torch.cuda.synchronize()
         n_chunks = 3
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for ci in range(n_chunks):
-            chunk(5 + ci)
+            chunk(5 + ci, ev=True)
         e1.record(stream)
         torch.cuda.synchronize()
         per_chunk = e0.elapsed_time(e1) / n_chunks
+        app_us = float(np.mean([a.elapsed_time(b) for a, b in app_ev])) * 1e3 / layers
         chunk_flops = layers * steps * 4.0 * D * H * nq * (S + W + CF) * TPF
         res["rolling_832x464_steady_chunk"] = {
             "ms_per_chunk": round(per_chunk, 2), "calls_per_chunk": layers * steps, "appends_per_chunk": layers,
             "tflops": round(chunk_flops / per_chunk / 1e9, 1),
+            "ms_per_chunk_attention": round(per_chunk - app_us * layers * 1e-3, 2),
+            "us_per_append": round(app_us, 2),
+            "append_frac_hbm": round(4.0 * nq * H * D * 2 / (app_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "ms_per_60_chunk_session_at_steady_rate": round(60 * per_chunk, 1)}
         del rc, pool, fin, ro
         torch.cuda.empty_cache()
@@ -661,7 +690,55 @@ def cpu_baseline(args, flops, nq, kv_tokens):
                              "ms_per_chunk_step_extrapolated": round(dt1 * 1e3 * nq / len(sample), 1)}
     except OSError:
         pass
+    # the same oracle on row samples of the other workloads (all threads), extrapolated to a
+    # whole call by allowed (query, key) pairs, and the rolling session by calls
+    res["other_workloads_extrapolated"] = cpu_other_workloads(args, res["value"])
     return res
+
+
+def cpu_other_workloads(args, step_tflops):
+    """Oracle rates on row samples of the MoBA training sequence and the 720p step, with the
+    whole call's time extrapolated from the sample's allowed pairs; the rolling session's
+    steady chunk (120 calls of the 832x464 step) from the whole-call rate above."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    out = {}
+    # MoBA: 21 + 21 + 21 frames of 1560 tokens, chunks of 3, 12 heads
+    tpf, frames, cf = 1560, 21, 3
+    n = 3 * frames * tpf
+    q, k, v = (synth.normal(n * H * D, seed=args.seed, kind=t).reshape(n, H, D) for t in (synth.Q, synth.K, synth.V))
+    rows = np.linspace(0, n - 1, 480).astype(np.int64)
+    pairs = sum(b - a for i in rows for a, b in oracle.moba_row_intervals(int(i), tpf, frames, cf))
+    t0 = time.perf_counter()
+    oracle.moba_attention(q, k, v, tpf, frames, cf, 1, 1 / math.sqrt(D), rows=rows)
+    dt = time.perf_counter() - t0
+    rate = 4.0 * D * H * pairs / dt / 1e12
+    total = 4.0 * D * H * 945 * tpf * tpf
+    out["moba_98280"] = {"tflops": round(rate, 5), "sample": f"{len(rows)} of {n} rows ({dt:.1f} s)",
+                         "s_per_call_extrapolated": round(total / rate / 1e12, 1)}
+    del q, k, v
+    # 720p: 14 resident frames + the 14400-token chunk (64800 keys), 24 heads
+    tpf, heads = 3600, 24
+    nq, nk = CF * tpf, (S + W + CF) * tpf
+    q = synth.normal(nq * heads * D, seed=args.seed, kind=synth.Q).reshape(nq, heads, D)
+    k = synth.normal(nk * heads * D, seed=args.seed, kind=synth.K).reshape(nk, heads, D)
+    v = synth.normal(nk * heads * D, seed=args.seed, kind=synth.V).reshape(nk, heads, D)
+    rows = np.linspace(0, nq - 1, 160).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attend(q[rows], k, v, [[(0, nk)]] * len(rows), 1 / math.sqrt(D))
+    dt = time.perf_counter() - t0
+    rate = 4.0 * D * heads * len(rows) * nk / dt / 1e12
+    out["720p_self"] = {"tflops": round(rate, 5), "sample": f"{len(rows)} of {nq} rows x {heads} heads against "
+                                                             f"all {nk} keys ({dt:.1f} s)",
+                        "s_per_call_extrapolated": round(4.0 * D * heads * nq * nk / rate / 1e12, 1)}
+    del q, k, v
+    call = 4.0 * D * H * CF * TPF * (S + W + CF) * TPF
+    out["rolling_832x464_steady_chunk"] = {"s_per_chunk_extrapolated": round(120 * call / step_tflops / 1e12, 1),
+                                           "from": "120 calls at the whole-call rate of the 832x464 step"}
+    return out
 
 
 def _cpu_model():

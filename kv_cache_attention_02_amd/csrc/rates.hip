@@ -1,9 +1,10 @@
 // Reference rates for the benchmark (measurement code, not part of the C ABI
 // of include/wmk.h): the bf16 matrix-core rate that a long stream of
-// independent v_mfma_f32_32x32x16_bf16 instructions reaches on this device.
-// The attention kernels' fraction of peak is also reported against this
+// independent v_mfma_f32_32x32x16_bf16 instructions reaches on this device
+// (the attention kernels' fraction of peak is also reported against this
 // measured rate, which includes the shader clock the chip holds under a
-// sustained matrix-core load.
+// sustained matrix-core load), and the rate of fp32 atomic adds in the
+// pattern of a dQ accumulation (the cost a fused attention backward would pay).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,9 +64,36 @@ __global__ __launch_bounds__(kThreads) void mfma_bf16_rate_kernel(int iters, flo
     sink[(size_t)blockIdx.x * kThreads + lane] = s;
 }
 
+// fp32 atomic adds without return in the pattern a fused attention backward
+// would accumulate dQ with: each workgroup adds a 64-row x 128-dim fp32 block
+// (row stride heads x 128) at a pseudo-random 64-row tile of one head.
+__global__ __launch_bounds__(512) void atomic_add_rate_kernel(float* acc, int n_tiles, int heads, int rounds) {
+    const int t = threadIdx.x;
+    const int head = blockIdx.x % heads;
+    for (int r = 0; r < rounds; ++r) {
+        const int tile = (int)(mix((uint32_t)blockIdx.x * 977u + (uint32_t)r) % (uint32_t)n_tiles);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int e = i * 512 + t;  // element of the 64 x 128 block
+            float* p = acc + ((size_t)(tile * 64 + (e >> 7)) * heads + head) * 128 + (e & 127);
+            __hip_atomic_fetch_add(p, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Enqueue `blocks` workgroups of atomic_add_rate_kernel over acc, a [n_tiles * 64]
+// [heads][128] fp32 buffer; each workgroup adds `rounds` blocks of 32 KiB.
+// Returns the launch status (hipError_t as int).
+__attribute__((visibility("default"))) int wmk_rate_atomic_add_f32(float* acc, int n_tiles, int heads, int blocks,
+                                                                   int rounds, hipStream_t s) {
+    if (acc == nullptr || n_tiles <= 0 || heads <= 0 || blocks <= 0 || rounds <= 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(atomic_add_rate_kernel, dim3(blocks), dim3(512), 0, s, acc, n_tiles, heads, rounds);
+    return (int)hipGetLastError();
+}
 
 // Enqueue `blocks` workgroups of 4 waves, each wave running iters * 4 bf16
 // 32x32x16 MFMAs (iters a positive multiple of 4); sink receives blocks * 256
