@@ -219,8 +219,10 @@ size_t wmk_attention_qk8_workspace_bytes(const wmk_head_desc* hd, int32_t q_toke
  * speed-up page, step table, "Attention" row: an INT8-QK^T SageAttention
  * kernel replaces FlashAttention-2; roofline table, "SageAttention" row; here
  * the operands are quantized to FP8 for the CDNA4 matrix cores).
- * Per head, Q is cut into blocks of 32 rows and the keys -- cache slots in
- * slot order, then the segments -- into tiles of 64; per block, in fp32:
+ * Per head, Q is cut into blocks of 32 rows and the keys -- the resident
+ * frames in time order (sinks, then the window, oldest first), then the
+ * segments -- into tiles of 64, so the blocks depend only on which frames are
+ * resident, not on where the ring has wrapped; per block, in fp32:
  * scale = max|x| / 448, code = e4m3(clamp(x * 448 / max|x|, +-448)), nearest
  * even (all zero: scale 0, codes 0).  Softmax, P (bf16) and P V (bf16, fp32
  * accumulate) are as in the plain path.
