@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--step-profile", action="store_true",
                     help="run the 832x464 call on the step-profile build of the library (libwmk_stepprof.so: "
                          "per-wave shader cycles of each phase of a 64-key step) and print the per-step budget")
+    ap.add_argument("--profile-workload", default="832x464", choices=["832x464", "720p_cross"],
+                    help="call profiled by --step-profile: the 832x464 step, or the 720p chunk's cross-attention "
+                         "(14400 queries x 24 heads over a 512-token environment and a 512-token local prompt)")
     ap.add_argument("--skip-rates", action="store_true",
                     help="skip the reference rates (MFMA microbenchmark, device-to-device copy)")
     return ap.parse_args()
@@ -118,50 +121,69 @@ def rolling_appends(wmk, synth, torch, fill, stream, reps=4):
     return us, layers * reps
 
 
-def step_profile(wmk, synth, torch, np, fill, stream, flops):
-    """The 832x464 call on the step-profile build: per wave, the shader cycles of each phase
-    of its 64-key steps -- [A] (S^T of the next tile on the matrix core beside this tile's
+def step_profile(wmk, synth, torch, np, fill, stream, flops, workload="832x464"):
+    """A call on the step-profile build: per wave, the shader cycles of each phase of its
+    64-key steps -- [A] (S^T of the next tile on the matrix core beside this tile's
     second-half weights), [B] (P V beside the next tile's row max and first-half weights),
     the wait for the step's own direct loads, the barrier, and the issue code before [A] --
-    averaged per step, over the 256 full units and over the split tail's pieces; waves
-    0-3 and 4-7 (the two waves of each SIMD) separately; and the shader clock from the
-    same span on the 100 MHz real-time counter."""
+    averaged per step, over the full units and over the split tail's pieces; waves 0-3 and
+    4-7 (the two waves of each SIMD) separately; the unit's fill (entry to the first step);
+    and the shader clock from the same span on the 100 MHz real-time counter.
+    workload: the 832x464 step, or the 720p chunk's cross-attention."""
     import ctypes
-    nq = CF * TPF
-    cache = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S, window_frames=W,
-                      chunk_frames=CF)
-    for c in range(4):
-        cache.append_evict(0, fill((nq, H, D), chunk=c, step=4, kind=synth.KFIN),
-                           fill((nq, H, D), chunk=c, step=4, kind=synth.VFIN), CF)
-    q, k, v = (fill((nq, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
+    if workload == "720p_cross":
+        tpf, heads = 3600, 24
+        nq = CF * tpf
+        q = fill((nq, heads, D), chunk=4, kind=synth.Q)
+        segs = [(fill((512, heads, D), kind=synth.KENV), fill((512, heads, D), kind=synth.VENV)),
+                (fill((512, heads, D), chunk=2, kind=synth.KLOC), fill((512, heads, D), chunk=2, kind=synth.VLOC))]
+        cache = None
+        flops = 4.0 * D * heads * nq * 1024
+    else:
+        nq = CF * TPF
+        cache = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
+                          window_frames=W, chunk_frames=CF)
+        for c in range(4):
+            cache.append_evict(0, fill((nq, H, D), chunk=c, step=4, kind=synth.KFIN),
+                               fill((nq, H, D), chunk=c, step=4, kind=synth.VFIN), CF)
+        q, k, v = (fill((nq, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
+        segs = [(k, v)]
     out = torch.empty_like(q)
     for _ in range(5):
-        wmk.chunk_attention(cache, 0, q, [(k, v)], out=out)
+        wmk.chunk_attention(cache, 0, q, segs, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    wmk.chunk_attention(cache, 0, q, [(k, v)], out=out)
+    wmk.chunk_attention(cache, 0, q, segs, out=out)
     e1.record(stream)
     torch.cuda.synchronize()
     lib = wmk.load()
     lib.wmk_step_profile_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    buf = np.zeros((4096 * 8, 9), np.uint64)
+    buf = np.zeros((4096 * 8, 16), np.uint64)
     assert lib.wmk_step_profile_read(buf.ctypes.data, buf.nbytes) == 0
-    wg = buf[:512 * 8].astype(np.float64).reshape(512, 8, 9)
+    wg = buf.astype(np.float64).reshape(4096, 8, 16)
+    used = wg[:, :, 5].sum(axis=1) > 0
+    piece = (buf.reshape(4096, 8, 16)[:, 0, 7] & np.uint64(255)) != np.uint64(255)
     names = ["A_qk_next_and_weights", "B_pv_and_next_max_weights", "wait_own_loads", "barrier", "issue_before_A"]
-    res = {"library": "libwmk_stepprof.so", "call_ms": round(e0.elapsed_time(e1), 4),
+    res = {"library": "libwmk_stepprof.so", "workload": workload, "call_ms": round(e0.elapsed_time(e1), 4),
            "call_tflops": round(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)}
-    for label, sl in (("full_units", slice(0, 256)), ("split_pieces", slice(256, 512))):
-        x = wg[sl]
-        part = {}
+    for label, sel in (("full_units", used & ~piece), ("split_pieces", used & piece)):
+        if not sel.any():
+            continue
+        x = wg[sel]
+        part = {"workgroups": int(sel.sum())}
         for waves, tag in ((slice(0, 8), "all_waves"), (slice(0, 4), "waves_0_3"), (slice(4, 8), "waves_4_7")):
-            y = x[:, waves].reshape(-1, 9)
+            y = x[:, waves].reshape(-1, 16)
             y = y[y[:, 5] > 0]
             per = {nm: round(float(np.mean(y[:, i] / y[:, 5])), 1) for i, nm in enumerate(names)}
             per["phases_sum"] = round(sum(per.values()), 1)
             per["cycles_per_step_span"] = round(float(np.mean(y[:, 6] / y[:, 5])), 1)
             if tag == "all_waves":
                 per["steps_per_wave"] = round(float(np.mean(y[:, 5])), 1)
+                per["fill_cycles_entry_to_first_step"] = round(float(np.mean(y[:, 9])), 1)
+                per["fill_parts"] = {nm: round(float(np.mean(y[:, 10 + i])), 1) for i, nm in enumerate(
+                    ["setup_and_q_loads_issued", "first_tiles_issued_and_waited", "barrier_1", "first_scores_and_weights",
+                     "barrier_2", "of_setup_until_the_unit_is_known"])}
                 per["shader_clock_GHz"] = round(float(np.mean(y[:, 6] / (y[:, 8] * 10.0))), 3)
             part[tag] = per
         res[label] = part
@@ -282,7 +304,7 @@ def main():
     append_bytes = 2.0 * 2 * nq * H * D * 2              # K + V chunk, read + write
 
     if args.step_profile:
-        print(json.dumps(step_profile(wmk, synth, torch, np, fill, stream, flops)))
+        print(json.dumps(step_profile(wmk, synth, torch, np, fill, stream, flops, args.profile_workload)))
         return
 
     if args.append_only:

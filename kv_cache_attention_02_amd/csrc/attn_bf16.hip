@@ -67,12 +67,14 @@ namespace wmk {
 // cycles (s_memtime) spent in each phase of the key-tile steps, summed over the
 // launch -- [A], [B], the wait for the step's own direct loads, the barrier and
 // the issue code before [A] -- plus the step count, the span from the first
-// step's start to the last step's end, the unit, and that span on the 100 MHz
-// real-time counter (s_memrealtime), which gives the shader clock.  Read back with
+// step's start to the last step's end, the unit, that span on the 100 MHz
+// real-time counter (s_memrealtime), which gives the shader clock, and the
+// cycles from the kernel's entry to the first step (the unit's fill: Q
+// fragments, the first tiles, the first scores) and its parts.  Read back with
 // wmk_step_profile_read after the launch.  Each timestamp is a scalar memory
 // read the following code waits on, so the profiled kernel runs a few percent
 // slower than the product build.
-__device__ unsigned long long g_step_prof[4096 * 8][9];
+__device__ unsigned long long g_step_prof[4096 * 8][16];
 extern "C" __attribute__((visibility("default"))) int wmk_step_profile_read(void* host, size_t bytes) {
     return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_step_prof), bytes, 0, hipMemcpyDeviceToHost);
 }
@@ -480,6 +482,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     const Buf<D> vb0 = mkbuf(v0p0, v0p1), vb1 = mkbuf(v1p0, v1p1);
 
     // ---- which unit (head, q-tile) and which key-tile range this workgroup runs
+    [[maybe_unused]] uint64_t pc_entry = 0;
+    WMK_STAMP(pc_entry);
     const int32_t b = blockIdx.x;
     const int32_t full_units = p.n_units - p.split_units;
     int32_t u, piece = -1;
@@ -511,22 +515,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         qt = u % p.n_qtiles;
     }
     const int32_t r0 = qt * BQ, r1 = min(r0 + BQ, c.q_tokens);
-    const TileRanges tr = tile_ranges(c, r0, r1);
-    int32_t it0 = 0, it1 = tr.total;
-    if (piece >= 0) {
-        it0 = (int32_t)((int64_t)tr.total * piece / p.splits);
-        it1 = (int32_t)((int64_t)tr.total * (piece + 1) / p.splits);
-    }
-
-    // ---- per-lane query row and its allowed key ranges
+    [[maybe_unused]] uint64_t fl0 = 0;
+    WMK_STAMP(fl0);  // the unit is known: the kernel arguments have arrived
+    // ---- per-lane query row; its Q fragments are loaded first, so that their
+    // memory latency overlaps the planning below (tile ranges, row ranges)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
     const int l32 = lane & 31, h = lane >> 5;
     const int32_t row = r0 + wave * 32 + l32;
     const bool row_ok = row < c.q_tokens;
     const bool wave_has_rows = (r0 + wave * 32) < c.q_tokens;
-    int32_t lo0, hi0, lo1, hi1;
-    row_ranges(c, row, lo0, hi0, lo1, hi1);
     const int64_t stride = (int64_t)c.heads * D;
 
     // Q^T fragments (B operand): lane owns query l32, dims ds*16 + h*8 .. +7
@@ -554,6 +552,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             qf[ds] = __builtin_bit_cast(bf16x8, raw);
         }
     }
+
+    const TileRanges tr = tile_ranges(c, r0, r1);
+    int32_t it0 = 0, it1 = tr.total;
+    if (piece >= 0) {
+        it0 = (int32_t)((int64_t)tr.total * piece / p.splits);
+        it1 = (int32_t)((int64_t)tr.total * (piece + 1) / p.splits);
+    }
+
+    int32_t lo0, hi0, lo1, hi1;
+    row_ranges(c, row, lo0, hi0, lo1, hi1);
 
     f32x16 o[C::DB];
 #pragma unroll
@@ -655,6 +663,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     auto k8_src = [&](int32_t tile) __attribute__((always_inline)) {
         return p.k8 + ((size_t)tile * c.heads + head) * kTile8;
     };
+    [[maybe_unused]] uint64_t fl1 = 0, fl2 = 0, fl3 = 0, fl4 = 0, fl5 = 0;
+    WMK_STAMP(fl1);
     if (it0 < it1) {
         if constexpr (Q8) {
             dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane, kb0.part[0] + wave * 1024);
@@ -673,7 +683,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
+        WMK_STAMP(fl2);
         __syncthreads();
+        WMK_STAMP(fl3);
         if (wave_has_rows) {
             if constexpr (Q8) qk_tile8(kb0.part[0], qf8, k8o, s);
             else qk_tile<D>(kb0, qf, la, s);
@@ -685,7 +697,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             pf0[1] = weights(I0{}, I1{}, m_use, lsum);
             l_run = lsum;
         }
+        WMK_STAMP(fl4);
         __syncthreads();  // K(it0) is read; the first iteration refills its buffer
+        WMK_STAMP(fl5);
     }
     kcu = vcu;
     advance(kcu, c, tr, it0 + 2, row_bytes, head_off);
@@ -968,6 +982,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         for (int i = 0; i < 7; ++i) e[i] = prof[i];
         e[7] = (unsigned long long)head << 32 | (unsigned long long)qt << 8 | (unsigned long long)(piece < 0 ? 255 : piece);
         e[8] = real_last - real_first;
+        e[9] = prof_first - pc_entry;
+        e[10] = fl1 - pc_entry;  // unit and ranges, Q fragment loads issued
+        e[15] = fl0 - pc_entry;  // of which: until the unit is known (kernel arguments)
+        e[11] = fl2 - fl1;       // first tiles issued, wait for them and for Q
+        e[12] = fl3 - fl2;       // barrier
+        e[13] = fl4 - fl3;       // first S^T, its max and first weights
+        e[14] = fl5 - fl4;       // barrier
     }
 #endif
     const float l_tot = pair_sum(l_run);
