@@ -523,6 +523,57 @@ def attention_backward(q, k, v, dout, mask, scale):
     return dq, dk, dv
 
 
+def attention_key_gradients(q, k, v, dout, row_intervals, keys, scale, block=1024):
+    """Exact (fp64) dk and dv at the key rows ``keys`` only, for the masked attention in
+    which query row i may attend the half-open key ranges ``row_intervals(i)`` -- the same
+    derivative as ``attention_backward``, without a dense mask: for the query rows that
+    attend a listed key, each row's softmax (its log-sum-exp, its output O and
+    D = dO . O) is formed over its own allowed keys, and then
+    dv_j = sum_i P_ij dO_i,  dk_j = scale sum_i P_ij (dO_i . v_j - D_i) q_i.
+    Rows are taken in runs that share their intervals (a MoBA chunk, for instance).
+    q, k, v, dout: [n][H][D] (float32 or bf16 bits).  Returns (dk, dv), each
+    [len(keys)][H][D] fp64, in the order of ``keys``."""
+    q, k, v, do = (widen(x) for x in (q, k, v, dout))
+    n, H, D = q.shape
+    keys = np.asarray(keys, dtype=np.int64)
+    dk = np.zeros((keys.size, H, D), np.float64)
+    dv = np.zeros((keys.size, H, D), np.float64)
+    runs = []
+    for i in range(n):
+        ivs = tuple((int(a), int(b)) for a, b in row_intervals(i) if b > a)
+        if runs and runs[-1][2] == ivs:
+            runs[-1][1] = i + 1
+        else:
+            runs.append([i, i + 1, ivs])
+    for r0, r1, ivs in runs:
+        if not ivs:
+            continue
+        allowed = np.concatenate([np.arange(a, b) for a, b in ivs])
+        hit = np.isin(keys, allowed)
+        if not hit.any():
+            continue
+        jpos = np.searchsorted(allowed, keys[hit])
+        for hh in range(H):
+            K = k[allowed, hh].astype(np.float64)
+            V = v[allowed, hh].astype(np.float64)
+            VJ = V[jpos]
+            for b0 in range(r0, r1, block):
+                b1 = min(b0 + block, r1)
+                Q = q[b0:b1, hh].astype(np.float64)
+                dO = do[b0:b1, hh].astype(np.float64)
+                s = (Q @ K.T) * scale
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                l = e.sum(axis=1, keepdims=True)
+                O = (e @ V) / l
+                Dsum = (dO * O).sum(axis=1, keepdims=True)
+                P = e[:, jpos] / l
+                dS = P * (dO @ VJ.T - Dsum)
+                dv[hit, hh] += P.T @ dO
+                dk[hit, hh] += scale * (dS.T @ Q)
+    return dk, dv
+
+
 def moba_mask(tokens_per_frame, frames, chunk_frames, bidir_block=1):
     n = (2 + bidir_block) * frames * tokens_per_frame
     ivs = [moba_row_intervals(i, tokens_per_frame, frames, chunk_frames, bidir_block) for i in range(n)]

@@ -2,7 +2,10 @@
 dv) through the C ABI against the oracle: every element on small sequences
 (ragged frames, partial last chunk, with and without the bidirectional block),
 and at the full 98 280-token sequence sampled dq rows, the dk/dv of whole
-self-contained blocks (noisy chunk 0), and the column sums that softmax fixes."""
+self-contained blocks (noisy chunk 0), sampled dk/dv key rows of clean chunks 0
+and 3 (the longest walks of the dK/dV kernel) against the oracle's per-key
+backward, and the column sums that softmax fixes; every element of a
+12 600-token sequence with the same structure."""
 import math
 
 import numpy as np
@@ -132,7 +135,18 @@ def test_moba_backward_full_sequence(wmk):
     compare_grad(gk[blk][:, heads], rk, "dk of noisy chunk 0")
     compare_grad(gv[blk][:, heads], rv, "dv of noisy chunk 0")
     compare_grad(gq[blk][:, heads], rq, "dq of noisy chunk 0")
-    # (c) softmax invariants over the whole sequence: sum_j dk_j = 0, sum_j dv_j = sum_i dout_i
+    # (c) sampled key rows with the longest walks: clean chunk 0 (read by the clean rows of all
+    # 7 chunks and the noisy rows of chunks 1-6: 60 840 rows, ~950 query tiles), clean chunk 3,
+    # and a noisy key -- exact dk, dv from the oracle's per-key backward (each attending row's
+    # softmax over its own allowed keys)
+    keys = np.array([0, 1, 2345, cl - 1, 3 * cl, 3 * cl + 2000, L + 2 * cl + 17])
+    say("  oracle per-key backward")
+    sub = lambda x: np.ascontiguousarray(x[:, heads])
+    rk, rv = oracle.attention_key_gradients(sub(q), sub(k), sub(v), sub(do),
+                                            lambda i: oracle.moba_row_intervals(i, tpf, frames, cf), keys, scale)
+    compare_grad(gk[keys][:, heads], rk, "dk of sampled keys (clean chunks 0 and 3, noisy chunk 2)")
+    compare_grad(gv[keys][:, heads], rv, "dv of sampled keys (clean chunks 0 and 3, noisy chunk 2)")
+    # (d) softmax invariants over the whole sequence: sum_j dk_j = 0, sum_j dv_j = sum_i dout_i
     dk64, dv64 = as_f32(gk).astype(np.float64), as_f32(gv).astype(np.float64)
     do64 = as_f32(do).astype(np.float64)
     assert np.abs(dk64.sum(axis=0)).max() <= 1e-2 * np.abs(dk64).sum(axis=0).max()

@@ -912,3 +912,25 @@ def test_lse_matches_c_probabilities():
     s = np.einsum("ihd,jhd->hij", q.astype(np.float64), k.astype(np.float64)) * 0.3
     p = np.where(mask[None], np.exp(s - lse[:, :, None]), 0.0)
     np.testing.assert_allclose(p.transpose(1, 0, 2), probs, atol=1e-14)
+
+
+
+@pytest.mark.parametrize("tpf,frames,cf,bidir", [(4, 6, 2, 1), (7, 5, 3, 0), (5, 4, 1, 1)])
+def test_key_gradients_match_the_dense_backward(tpf, frames, cf, bidir):
+    """The streamed per-key gradients (each row's softmax over its own allowed keys, rows in
+    runs of equal intervals) equal the dense masked backward's dk and dv rows."""
+    n = (2 + bidir) * frames * tpf
+    H, D = 2, 16
+    q, k, v, do = (_rand((n, H, D), 600 + i) for i in range(4))
+    rq, rk, rv = oracle.attention_backward(q, k, v, do, oracle.moba_mask(tpf, frames, cf, bidir), 0.3)
+    rng = np.random.default_rng(7)
+    keys = np.array(sorted(rng.choice(n, size=min(n, 17), replace=False)))
+    ivs = lambda i: oracle.moba_row_intervals(i, tpf, frames, cf, bidir)
+    gk, gv = oracle.attention_key_gradients(q, k, v, do, ivs, keys, 0.3, block=5)
+    np.testing.assert_allclose(gk, rk[keys], rtol=0, atol=1e-12 * max(1.0, np.abs(rk).max()))
+    np.testing.assert_allclose(gv, rv[keys], rtol=0, atol=1e-12 * max(1.0, np.abs(rv).max()))
+    # every key at once, in a shuffled order
+    allk = rng.permutation(n)
+    gk, gv = oracle.attention_key_gradients(q, k, v, do, ivs, allk, 0.3, block=64)
+    np.testing.assert_allclose(gk, rk[allk], rtol=0, atol=1e-12 * max(1.0, np.abs(rk).max()))
+    np.testing.assert_allclose(gv, rv[allk], rtol=0, atol=1e-12 * max(1.0, np.abs(rv).max()))
