@@ -523,6 +523,40 @@ def attention_backward(q, k, v, dout, mask, scale):
     return dq, dk, dv
 
 
+def attention_by_runs(q, k, v, row_intervals, scale, heads=None, block=1024):
+    """Masked softmax attention in fp64 with dense BLAS products, for checks of every row of
+    long sequences: rows are taken in runs that share their allowed key ranges
+    ``row_intervals(i)`` (a MoBA chunk, a chunk of queries over the whole cache), and each
+    block of a run attends its allowed keys as one dense, unmasked softmax (two passes: row
+    max, then exponentials, sums and weighted values).  A row with no key gets 0.
+    q: [nq][H][D], k, v: [nk][H][D] (float32 or bf16 bits); ``heads`` selects heads.
+    Returns fp64 [nq][len(heads)][D]."""
+    q, k, v = (widen(x) for x in (q, k, v))
+    heads = list(range(q.shape[1])) if heads is None else list(heads)
+    nq, D = q.shape[0], q.shape[2]
+    out = np.zeros((nq, len(heads), D), np.float64)
+    runs = []
+    for i in range(nq):
+        ivs = tuple((int(a), int(b)) for a, b in row_intervals(i) if b > a)
+        if runs and runs[-1][2] == ivs:
+            runs[-1][1] = i + 1
+        else:
+            runs.append([i, i + 1, ivs])
+    for r0, r1, ivs in runs:
+        if not ivs:
+            continue
+        allowed = np.concatenate([np.arange(a, b) for a, b in ivs])
+        for x, hh in enumerate(heads):
+            K = k[allowed, hh].astype(np.float64)
+            V = v[allowed, hh].astype(np.float64)
+            for b0 in range(r0, r1, block):
+                b1 = min(b0 + block, r1)
+                s = (q[b0:b1, hh].astype(np.float64) @ K.T) * scale
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                out[b0:b1, x] = (e @ V) / e.sum(axis=1, keepdims=True)
+    return out
+
+
 def attention_key_gradients(q, k, v, dout, row_intervals, keys, scale, block=1024):
     """Exact (fp64) dk and dv at the key rows ``keys`` only, for the masked attention in
     which query row i may attend the half-open key ranges ``row_intervals(i)`` -- the same

@@ -327,6 +327,11 @@ def test_moba_training_sequence_full_size(wmk):
     say(f"moba full size: oracle on {len(rows)} rows")
     ref = oracle.moba_attention(q, k, v, tpf, frames, cf, 1, 1 / math.sqrt(D), rows=rows)
     compare(got[rows], ref, BF16_MAX_ABS, BF16_REL_L2, "sampled rows")
+    # every row of one head (rows in runs of equal mask intervals, dense BLAS blocks)
+    say("moba full size: oracle on every row of head 5")
+    ref5 = oracle.attention_by_runs(q, k, v, lambda i: oracle.moba_row_intervals(i, tpf, frames, cf), 1 / math.sqrt(D),
+                                    heads=[5])
+    compare(got[:, [5]], ref5, BF16_MAX_ABS, BF16_REL_L2, "every row of head 5")
 
 
 # ----------------------------------------------------------------------------------------------
@@ -353,6 +358,12 @@ def test_720p_self_and_cross_attention(wmk):
     say(f"720p: oracle on {len(rows)} rows")
     ref = oracle.chunk_attention(cm, q, [(k, v)], 1 / math.sqrt(D), rows=rows)
     compare(from_dev(out)[rows], ref, BF16_MAX_ABS, BF16_REL_L2, "self, sampled rows")
+    # every row of head 13 over all 64 800 keys (the head's units include split-tail pieces)
+    say("720p: oracle on every row of head 13")
+    kc, vc = cm.logical_kv()
+    kall, vall = np.concatenate([kc, k]), np.concatenate([vc, v])
+    ref13 = oracle.attention_by_runs(q, kall, vall, lambda i: [(0, kall.shape[0])], 1 / math.sqrt(D), heads=[13])
+    compare(from_dev(out)[:, [13]], ref13, BF16_MAX_ABS, BF16_REL_L2, "self, every row of head 13")
     cache.close()
 
     # cross-attention: chunk 2 reads the shared environment prompt and its own local prompt
@@ -365,6 +376,10 @@ def test_720p_self_and_cross_attention(wmk):
     rows = sample_rows(nq, np.random.default_rng(3), k=64)
     ref = oracle.cross_attention(q, 2, ke, ve, kl, vl, 1 / math.sqrt(D), rows=rows)
     compare(from_dev(out)[rows], ref, BF16_MAX_ABS, BF16_REL_L2, "cross, sampled rows")
+    kx, vx = np.concatenate([ke] + kl), np.concatenate([ve] + vl)
+    ivx = oracle.cross_row_intervals(2, 512, 512)
+    refx = oracle.attention_by_runs(q, kx, vx, lambda i: ivx, 1 / math.sqrt(D), heads=[0, 23])
+    compare(from_dev(out)[:, [0, 23]], refx, BF16_MAX_ABS, BF16_REL_L2, "cross, every row of heads 0 and 23")
 
 
 # ----------------------------------------------------------------------------------------------

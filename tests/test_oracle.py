@@ -934,3 +934,26 @@ def test_key_gradients_match_the_dense_backward(tpf, frames, cf, bidir):
     gk, gv = oracle.attention_key_gradients(q, k, v, do, ivs, allk, 0.3, block=64)
     np.testing.assert_allclose(gk, rk[allk], rtol=0, atol=1e-12 * max(1.0, np.abs(rk).max()))
     np.testing.assert_allclose(gv, rv[allk], rtol=0, atol=1e-12 * max(1.0, np.abs(rv).max()))
+
+
+
+@pytest.mark.parametrize("tpf,frames,cf,bidir", [(4, 6, 2, 1), (7, 5, 3, 0)])
+def test_attention_by_runs_matches_the_c_core(tpf, frames, cf, bidir):
+    """The BLAS-blocked, run-by-run masked attention equals the C core row by row: MoBA
+    masks, the cross-attention training mask, and an unmasked call with a ragged block."""
+    n = (2 + bidir) * frames * tpf
+    H, D = 3, 16
+    q, k, v = (_rand((n, H, D), 700 + i) for i in range(3))
+    ivs = lambda i: oracle.moba_row_intervals(i, tpf, frames, cf, bidir)
+    a = oracle.attention_by_runs(q, k, v, ivs, 0.4, block=7)
+    b = oracle.attend(q, k, v, [ivs(i) for i in range(n)], 0.4)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    a = oracle.attention_by_runs(q, k, v, ivs, 0.4, heads=[2, 0], block=64)
+    np.testing.assert_allclose(a, b[:, [2, 0]], rtol=0, atol=1e-12)
+    xi = lambda i: oracle.cross_train_row_intervals(i, 9, 5, 4)
+    kx, vx = _rand((5 + 4 * (n // 9 + 1), H, D), 710), _rand((5 + 4 * (n // 9 + 1), H, D), 711)
+    a = oracle.attention_by_runs(q[:9 * (n // 9)], kx, vx, xi, 0.4, block=4)
+    b = oracle.attend(q[:9 * (n // 9)], kx, vx, [xi(i) for i in range(9 * (n // 9))], 0.4)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    a = oracle.attention_by_runs(q, k, v, lambda i: [(0, n)], 0.4, block=13)
+    np.testing.assert_allclose(a, oracle.attend(q, k, v, [[(0, n)]] * n, 0.4), rtol=0, atol=1e-12)
