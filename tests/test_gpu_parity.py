@@ -413,3 +413,39 @@ def test_moba_per_key_weights(wmk, tpf, frames, cf):
         bad = np.argwhere(err > 8e-3 * np.maximum(ref, 1e-3) + 2e-4)
         say(f"  keys {base}..{base + w - 1}: max weight error {err.max():.2e}, {len(bad)} bad (row, key) pairs")
         assert len(bad) == 0, f"first bad (row, key): {[(int(r), int(c) + base) for r, c in bad[:5]]}"
+
+
+# ----------------------------------------------------------------------------------------------
+# the binding's scratch is per (device, stream): two streams running split-tail calls at once
+# ----------------------------------------------------------------------------------------------
+
+def test_two_streams_split_tail_concurrently(wmk):
+    """Chunk attention with the split tail on two streams at once (different queries, one
+    cache): each stream gets its own scratch from the binding, so both outputs equal the
+    same calls made one after the other."""
+    import torch
+    S, W, cf, tpf, H, D = 6, 8, 4, 1508, 12, 128
+    cache = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=cf)
+    for c in range(4):
+        cache.append_evict(0, dev_fill((cf * tpf, H, D), seed=90, chunk=c, kind=synth.KFIN),
+                           dev_fill((cf * tpf, H, D), seed=90, chunk=c, kind=synth.VFIN), cf)
+    qs = [dev_fill((cf * tpf, H, D), seed=91 + i, kind=synth.Q) for i in range(2)]
+    k, v = dev_fill((cf * tpf, H, D), seed=93, kind=synth.K), dev_fill((cf * tpf, H, D), seed=93, kind=synth.V)
+    torch.cuda.synchronize()
+    say("two streams: serial references")
+    refs = [wmk.chunk_attention(cache, 0, q, [(k, v)]).clone() for q in qs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(qs[0]) for _ in range(2)]
+    say("two streams: concurrent calls")
+    for rep in range(3):
+        for i in range(2):
+            streams[i].wait_stream(torch.cuda.current_stream())
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                wmk.chunk_attention(cache, 0, qs[i], [(k, v)], out=outs[i], stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(outs[i].view(torch.int16), refs[i].view(torch.int16)), (rep, i)
+    cache.close()
