@@ -484,6 +484,38 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     // ---- which unit (head, q-tile) and which key-tile range this workgroup runs
     [[maybe_unused]] uint64_t pc_entry = 0;
     WMK_STAMP(pc_entry);
+    // The kernel arguments the unit's set-up reads, all loaded here: issued
+    // together they cost one round trip to the scalar cache, where loads left at
+    // their first use (inside the mask-mode and split branches) each waited for
+    // their own.
+    {
+        const int32_t a0 = p.n_units, a1 = p.split_units, a2 = p.splits, a3 = p.xcd_remap, a4 = p.n_groups,
+                      a5 = p.n_qtiles, a6 = c.q_tokens, a7 = c.heads, a8 = c.kv_total, a9 = c.kv.n,
+                      a10 = c.mask.mode, a11 = c.mask.part_len, a12 = c.mask.chunk_len, a13 = c.mask.parts,
+                      a14 = c.mask.env_len;
+        const uint32_t b0 = p.splits_div.mul, b1 = p.splits_div.shift, b2 = p.qtiles_div.mul,
+                       b3 = p.qtiles_div.shift, b4 = p.heads_div.mul, b5 = p.heads_div.shift,
+                       b6 = c.mask.part_div.mul, b7 = c.mask.part_div.shift, b8 = c.mask.chunk_div.mul,
+                       b9 = c.mask.chunk_div.shift;
+        const float sc = c.scale;
+        const void* qp = c.q;
+        constexpr int F = NS < kFewSeg ? NS : kFewSeg;  // the spans of the common calls
+        const void* sk[kFewSeg] = {};
+        const void* sv[kFewSeg] = {};
+        int32_t se[kFewSeg] = {};
+#pragma unroll
+        for (int x = 0; x < F; ++x) {
+            sk[x] = c.kv.k[x];
+            sv[x] = c.kv.v[x];
+            se[x] = c.kv.end[x];
+        }
+        asm volatile("" ::"s"(a0), "s"(a1), "s"(a2), "s"(a3), "s"(a4), "s"(a5), "s"(a6), "s"(a7), "s"(a8), "s"(a9),
+                     "s"(a10), "s"(a11), "s"(a12), "s"(a13), "s"(a14), "s"(b0), "s"(b1), "s"(b2), "s"(b3), "s"(b4),
+                     "s"(b5), "s"(b6), "s"(b7), "s"(b8), "s"(b9), "s"(sc), "s"(qp));
+        static_assert(kFewSeg == 5, "one asm operand per span field");
+        asm volatile("" ::"s"(sk[0]), "s"(sk[1]), "s"(sk[2]), "s"(sk[3]), "s"(sk[4]), "s"(sv[0]), "s"(sv[1]),
+                     "s"(sv[2]), "s"(sv[3]), "s"(sv[4]), "s"(se[0]), "s"(se[1]), "s"(se[2]), "s"(se[3]), "s"(se[4]));
+    }
     const int32_t b = blockIdx.x;
     const int32_t full_units = p.n_units - p.split_units;
     int32_t u, piece = -1;
@@ -496,14 +528,14 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             u = b;
         }
     } else {
-        const int32_t pb = b - full_units;
-        u = full_units + pb / p.splits;
-        piece = pb % p.splits;
+        const int32_t pb = b - full_units, pu = tiles::udiv(pb, p.splits_div);
+        u = full_units + pu;
+        piece = pb - pu * p.splits;
     }
     int32_t head, qt;
     if (p.n_groups > 0) {  // longest-first order of q-tiles, all heads of a q-tile together
-        const int32_t k = u / c.heads;
-        head = u % c.heads;
+        const int32_t k = tiles::udiv(u, p.heads_div);
+        head = u - k * c.heads;
         int32_t acc = 0;
         qt = 0;
         for (int g = 0; g < p.n_groups; ++g) {
@@ -511,8 +543,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             acc += p.grp_count[g];
         }
     } else {
-        head = u / p.n_qtiles;
-        qt = u % p.n_qtiles;
+        head = tiles::udiv(u, p.qtiles_div);
+        qt = u - head * p.n_qtiles;
     }
     const int32_t r0 = qt * BQ, r1 = min(r0 + BQ, c.q_tokens);
     [[maybe_unused]] uint64_t fl0 = 0;
@@ -556,8 +588,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     const TileRanges tr = tile_ranges(c, r0, r1);
     int32_t it0 = 0, it1 = tr.total;
     if (piece >= 0) {
-        it0 = (int32_t)((int64_t)tr.total * piece / p.splits);
-        it1 = (int32_t)((int64_t)tr.total * (piece + 1) / p.splits);
+        // tr.total * splits < 2^31 (the host caps the split count at total / 8)
+        it0 = tiles::udiv(tr.total * piece, p.splits_div);
+        it1 = tiles::udiv(tr.total * (piece + 1), p.splits_div);
     }
 
     int32_t lo0, hi0, lo1, hi1;

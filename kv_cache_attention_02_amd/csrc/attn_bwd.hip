@@ -169,7 +169,7 @@ __device__ __forceinline__ void col_ranges(const MaskShape& m, int32_t n, int32_
     lo0 = hi0 = lo1 = hi1 = 0;
     if (j >= n) return;
     const int32_t L = m.part_len, cl = m.chunk_len;
-    const int32_t part = j / L, c = (j - part * L) / cl;
+    const int32_t part = tiles::udiv(j, m.part_div), c = tiles::udiv(j - part * L, m.chunk_div);
     if (part == 0) {
         lo0 = c * cl; hi0 = L;
         lo1 = min(L + (c + 1) * cl, 2 * L); hi1 = m.parts > 1 ? 2 * L : lo1;
@@ -187,16 +187,16 @@ __device__ __forceinline__ tiles::TileRanges col_tile_ranges(const MaskShape& m,
     int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
     const int32_t L = m.part_len, cl = m.chunk_len;
     c1 = min(c1, n);
-    const int32_t pa = c0 / L, pb = (c1 - 1) / L;
     if (c1 > c0) {
+        const int32_t pa = udiv(c0, m.part_div), pb = udiv(c1 - 1, m.part_div);
         if (pa <= 0 && 0 <= pb) {  // clean keys: from the first key's chunk on, clean and (later) noisy rows
-            const int32_t ca = c0 / cl;
+            const int32_t ca = udiv(c0, m.chunk_div);
             set_tiles(l0, h0, ca * cl, L);
             if (m.parts > 1) set_tiles(l1, h1, min(L + (ca + 1) * cl, 2 * L), 2 * L);
         }
         if (pa <= 1 && 1 <= pb) {  // noisy keys: the noisy rows of their chunks
             const int32_t fa = max(c0, L) - L, fb = min(c1, 2 * L) - L - 1;
-            set_tiles(l2, h2, L + (fa / cl) * cl, L + min((fb / cl + 1) * cl, L));
+            set_tiles(l2, h2, L + udiv(fa, m.chunk_div) * cl, L + min((udiv(fb, m.chunk_div) + 1) * cl, L));
         }
         if (pa <= 2 && 2 <= pb) set_tiles(l3, h3, 2 * L, 3 * L);
     }

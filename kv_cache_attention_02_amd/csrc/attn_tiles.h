@@ -22,8 +22,11 @@ struct TileRanges {
 
 constexpr int32_t kNone = 0x7fffffff;  // empty slot
 
+// Key (or row) indices here are never negative: divide them as unsigned.
+__device__ __forceinline__ int32_t udiv(int32_t n, FastDiv d) { return (int32_t)fastdiv((uint32_t)n, d); }
+
 __device__ __forceinline__ void set_tiles(int32_t& l, int32_t& h, int32_t a, int32_t b) {
-    if (b > a) { l = a / BK; h = (b + BK - 1) / BK; }
+    if (b > a) { l = (int32_t)((uint32_t)a / BK); h = (int32_t)(((uint32_t)b + BK - 1) / BK); }
 }
 
 __device__ __forceinline__ void order(int32_t& al, int32_t& ah, int32_t& bl, int32_t& bh) {
@@ -80,19 +83,20 @@ __device__ __forceinline__ TileRanges tile_ranges(const Call& c, int32_t r0, int
     if (c.mask.mode == kMaskNone) {
         set_tiles(l0, h0, 0, c.kv_total);
     } else if (c.mask.mode == kMaskCross) {  // environment prompt + the local prompts of the tile's chunks
-        const int32_t ca = r0 / c.mask.part_len, cb = (r1 - 1) / c.mask.part_len;
+        const int32_t ca = udiv(r0, c.mask.part_div), cb = udiv(r1 - 1, c.mask.part_div);
         set_tiles(l0, h0, 0, c.mask.env_len);
         set_tiles(l1, h1, c.mask.env_len + ca * c.mask.chunk_len, c.mask.env_len + (cb + 1) * c.mask.chunk_len);
     } else {
         const int32_t L = c.mask.part_len, cl = c.mask.chunk_len;
-        const int32_t pa = r0 / L, pb = min((r1 - 1) / L, c.mask.parts - 1);
+        const FastDiv pd = c.mask.part_div, cd = c.mask.chunk_div;
+        const int32_t pa = udiv(r0, pd), pb = min(udiv(r1 - 1, pd), c.mask.parts - 1);
         if (pa <= 0 && 0 <= pb) {  // clean rows: block-causal prefix
             const int32_t fb = min(r1, L) - 1;
-            set_tiles(l0, h0, 0, min((fb / cl + 1) * cl, L));
+            set_tiles(l0, h0, 0, min((udiv(fb, cd) + 1) * cl, L));
         }
         if (pa <= 1 && 1 <= pb) {  // noisy rows: earlier clean chunks, own noisy chunk
             const int32_t fa = max(r0, L) - L, fb = min(r1, 2 * L) - L - 1;
-            const int32_t ka = fa / cl, kb = fb / cl;
+            const int32_t ka = udiv(fa, cd), kb = udiv(fb, cd);
             set_tiles(l1, h1, 0, kb * cl);
             set_tiles(l2, h2, L + ka * cl, L + min((kb + 1) * cl, L));
         }
@@ -119,13 +123,13 @@ __device__ __forceinline__ void row_ranges(const Call& c, int32_t row, int32_t& 
     lo1 = 0; hi1 = 0;
     if (c.mask.mode == kMaskNone || row >= c.q_tokens) { lo0 = 0; hi0 = c.kv_total; return; }
     if (c.mask.mode == kMaskCross) {
-        const int32_t ch = row / c.mask.part_len;
+        const int32_t ch = udiv(row, c.mask.part_div);
         lo0 = 0; hi0 = c.mask.env_len;
         lo1 = c.mask.env_len + ch * c.mask.chunk_len; hi1 = lo1 + c.mask.chunk_len;
         return;
     }
     const int32_t L = c.mask.part_len, cl = c.mask.chunk_len;
-    const int32_t part = row / L, r = row - part * L, k = r / cl;
+    const int32_t part = udiv(row, c.mask.part_div), r = row - part * L, k = udiv(r, c.mask.chunk_div);
     const int32_t e = min((k + 1) * cl, L);
     if (part == 0) { lo0 = 0; hi0 = e; }
     else if (part == 1) { lo0 = 0; hi0 = k * cl; lo1 = L + k * cl; hi1 = L + e; }

@@ -159,7 +159,10 @@ constexpr int kMinTilesPerPiece = 8;
 // Split the last, partly filled round of units over the whole GPU when the
 // caller gave enough workspace.  Returns the workspace bytes that split needs
 // (0 when the call gets no split whatever the workspace).
-size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* ws, size_t ws_bytes) {
+// kv_tiles: 64-key tiles of the whole key range, a bound on any unit's visits
+// (the kernel splits with 32-bit products visits x piece).
+size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, int32_t kv_tiles, void* ws,
+                  size_t ws_bytes) {
     p.split_units = 0;
     p.splits = 1;
     p.ws = nullptr;
@@ -170,6 +173,7 @@ size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, void* 
     const int32_t rounds = p.n_units / slots, tail = p.n_units % slots;
     if (rounds < 1 || tail == 0) return 0;
     int32_t splits = std::min<int32_t>(slots / tail, tiles_per_unit / kMinTilesPerPiece);
+    splits = std::min<int32_t>(splits, INT32_MAX / std::max(kv_tiles, 1));
     if (splits < 2) return 0;
     const size_t need = wmk::attn_bf16_split_ws_bytes(head_dim, tail, splits);
     // (the pieces store 16-byte vectors: a misaligned workspace is not used)
@@ -274,15 +278,19 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
             // every q-tile visits the same number of key tiles: the whole key
             // range, or (cross mask) the environment prompt plus its chunks'
             // local prompts
-            int32_t tiles = (call.kv_total + kBK - 1) / kBK;
+            const int32_t kv_tiles = (int32_t)(((int64_t)call.kv_total + kBK - 1) / kBK);
+            int32_t tiles = kv_tiles;
             if (call.mask.mode == wmk::kMaskCross)
                 tiles = (call.mask.env_len + kBK - 1) / kBK + (call.mask.chunk_len + kBK - 1) / kBK;
             p.xcd_remap = 1;
-            const size_t need = plan_split(p, call.head_dim, tiles, ws, ws_bytes);
+            const size_t need = plan_split(p, call.head_dim, tiles, kv_tiles, ws, ws_bytes);
             if (strict_ws && need > ws_bytes)
                 return fail(WMK_ERR_CAPACITY, "the split tail of this call needs %zu bytes of scratch; the library "
                             "holds %zu", need, ws_bytes);
         }
+        p.heads_div = wmk::make_fastdiv((uint32_t)std::max(call.heads, 1));
+        p.qtiles_div = wmk::make_fastdiv((uint32_t)std::max(p.n_qtiles, 1));
+        p.splits_div = wmk::make_fastdiv((uint32_t)std::max(p.splits, 1));
         if (qk8 != nullptr) {
             p.k8 = qk8->k8;
             p.k8_scale = qk8->k8_scale;
@@ -487,6 +495,7 @@ wmk_status moba_call(const wmk_moba_desc* m, const wmk_head_desc* hd, const void
     call.mask.part_len = (int32_t)L;
     call.mask.chunk_len = std::min(m->chunk_frames, m->frames) * m->tokens_per_frame;
     call.mask.parts = 2 + m->bidir_block;
+    wmk::set_mask_divisors(call.mask);
     return WMK_OK;
 }
 
@@ -772,6 +781,7 @@ wmk_status wmk_cross_attention_train(const wmk_xattn_desc* x, const wmk_head_des
     call.mask.chunk_len = x->local_tokens;
     call.mask.parts = x->chunks;
     call.mask.env_len = x->env_tokens;
+    wmk::set_mask_divisors(call.mask);
     return run_attention(call, hd->dtype, workspace, workspace_bytes, stream);
 }
 

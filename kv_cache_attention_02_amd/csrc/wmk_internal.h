@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
+
 namespace wmk {
 
 constexpr int kMaxSeg = 16;       // spans of one call: cache runs + caller segments
@@ -45,7 +47,16 @@ struct MaskShape {
     int32_t chunk_len;
     int32_t parts;
     int32_t env_len;
+    FastDiv part_div;   // division by part_len (set with set_mask_divisors)
+    FastDiv chunk_div;  // division by chunk_len
 };
+
+// Fill in the divisors of a mask (a length of 0, which no kernel divides by,
+// gets the divisor 1).
+inline void set_mask_divisors(MaskShape& m) {
+    m.part_div = make_fastdiv(m.part_len > 1 ? (uint32_t)m.part_len : 1u);
+    m.chunk_div = make_fastdiv(m.chunk_len > 1 ? (uint32_t)m.chunk_len : 1u);
+}
 
 template <int N>
 struct AttnCallN {
@@ -67,14 +78,16 @@ using AttnCall = AttnCallN<kMaxSeg>;
 struct AttnPlan {
     int32_t n_qtiles;       // ceil(q_tokens / attn_bf16_block_q())
     int32_t n_units;        // n_qtiles * heads
-    int32_t n_groups;       // > 0: q-tiles visited in this group order (longest first)
-    int32_t grp_start[kMaxGroups];
-    int32_t grp_count[kMaxGroups];
+    int32_t n_groups;       // > 0: q-tiles visited in this group order (longest first, grp_* below)
     int32_t xcd_remap;      // 1: keep consecutive units of one head on one XCD
     // split tail: the last `split_units` units (in launch order) run as
     // `splits` pieces each over disjoint key-tile ranges, merged in-kernel.
     int32_t split_units;
     int32_t splits;
+    // the same counts as multiply-shift divisors: heads (c.heads), n_qtiles, splits
+    FastDiv heads_div;
+    FastDiv qtiles_div;
+    FastDiv splits_div;
     void* ws;               // workspace for the split tail (may be NULL when split_units == 0)
     // FP8 QK^T (all NULL for the bf16 product): e4m3 codes of Q in blocks of 32
     // rows and of K in blocks of 64 keys (one tile, stored in the kernel's LDS
@@ -84,6 +97,9 @@ struct AttnPlan {
     const float* q8_scale;
     const uint8_t* k8;
     const float* k8_scale;
+    // the group order (last: the kernel reads the fields above at its start)
+    int32_t grp_start[kMaxGroups];
+    int32_t grp_count[kMaxGroups];
 };
 
 // bf16 MFMA attention.  Returns the launch status.

@@ -670,3 +670,65 @@ def test_noalloc_plans_like_the_workspace_entry(lib, dry):
         assert lib.wmk_chunk_attention_noalloc(*args, None) == status
     assert len(dry.read_text().splitlines()) == n_before
     lib.wmk_cache_destroy(h)
+
+
+_FASTDIV_CHECK = r"""
+#include "fastdiv.h"
+#include <cstdio>
+#include <random>
+int main() {
+    using namespace wmk;
+    std::mt19937_64 g(7);
+    long bad = 0, n_checked = 0;
+    auto check = [&](uint32_t n, uint32_t d, FastDiv f) {
+        ++n_checked;
+        if (fastdiv(n, f) != n / d) { if (bad < 5) printf("wrong: %u / %u\n", n, d); ++bad; }
+    };
+    // every divisor up to 70000: around the first 64 multiples, near 2^31 and at random
+    for (uint32_t d = 1; d <= 70000; ++d) {
+        const FastDiv f = make_fastdiv(d);
+        for (uint64_t k = 0; k < 64; ++k)
+            for (int e = -1; e <= 1; ++e) { const int64_t n = (int64_t)(k * d) + e; if (n >= 0) check((uint32_t)n, d, f); }
+        const int64_t top = (int64_t)(((1ull << 31) - 1) / d * d);
+        for (int e = -1; e <= 1; ++e) if (top + e < (1ll << 31)) check((uint32_t)(top + e), d, f);
+        for (int r = 0; r < 32; ++r) check((uint32_t)(g() & 0x7fffffffu), d, f);
+    }
+    // random divisors below 2^31, at random dividends, 2^31 - 1 and multiples +- 1
+    for (int r = 0; r < 1000000; ++r) {
+        const uint32_t d = 1 + (uint32_t)(g() % 0x7ffffffeu);
+        const FastDiv f = make_fastdiv(d);
+        check((uint32_t)(g() & 0x7fffffffu), d, f);
+        check(0x7fffffffu, d, f);
+        const uint32_t q = (uint32_t)(g() % (0x80000000ull / d));
+        check(q * d, d, f);
+        if (q * d) check(q * d - 1, d, f);
+    }
+    // the divisors of the workloads (tokens per frame, chunk and part lengths, heads), every n < 2^24
+    for (uint32_t d : {1u, 3u, 12u, 24u, 64u, 1508u, 1560u, 3600u, 4680u, 32760u})
+        { const FastDiv f = make_fastdiv(d); for (uint32_t n = 0; n < (1u << 24); ++n) check(n, d, f); }
+    printf("%ld %ld\n", n_checked, bad);
+    return bad != 0;
+}
+"""
+
+
+def test_fast_division_is_exact(tmp_path):
+    """The kernels' multiply-shift division (csrc/fastdiv.h, Granlund-Montgomery) equals
+    integer division for every dividend below 2^31: checked on the host, with the same
+    constexpr code the kernels compile, over all divisors to 70000 at the multiples'
+    edges, a million random divisors, and every dividend below 2^24 for the workloads'
+    divisors."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "fastdiv_check.cpp"
+    src.write_text(_FASTDIV_CHECK)
+    exe = tmp_path / "fastdiv_check"
+    subprocess.run([gxx, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "kv_cache_attention_02_amd", "csrc"),
+                    str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout
+    checked, wrong = map(int, r.stdout.split()[-2:])
+    assert wrong == 0 and checked > 100_000_000
