@@ -200,8 +200,9 @@ wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head
  * array needs clearing between calls.  Arguments, layout and ownership as
  * for wmk_chunk_attention.
  * Errors: as wmk_chunk_attention; a split tail needing more than the array
- * (more than 256 pieces: a device with more than 256 resident attention
- * workgroups) -> WMK_ERR_CAPACITY; the array's address not available ->
+ * (more pieces than a 256-CU MI355X has resident attention workgroups: 256
+ * pieces of 256 query rows, or 512 of 128 rows for short key walks) ->
+ * WMK_ERR_CAPACITY; the array's address not available ->
  * WMK_ERR_HIP.  Nothing is enqueued on error. */
 wmk_status wmk_chunk_attention_noalloc(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,
                                        int32_t q_tokens, const wmk_kv_segment* seg, int32_t n_seg, void* out,

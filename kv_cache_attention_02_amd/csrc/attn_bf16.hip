@@ -98,16 +98,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int NW = 8;        // waves per workgroup
-constexpr int NT = NW * 64;  // threads per workgroup
-constexpr int BQ = NW * 32;  // query rows per workgroup
 constexpr int BK = tiles::BK; // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units (weights stay <= 256)
 
-template <int D>
+// D: head dim; NW: waves per workgroup (8: one workgroup per CU; 4: two per CU,
+// for calls of short units, where one workgroup's fill runs beside the other's steps)
+template <int D, int NW>
 struct Cfg {
+    static constexpr int NT = NW * 64;                  // threads per workgroup
+    static constexpr int BQ = NW * 32;                  // query rows per workgroup
     static constexpr int CPR = D / 8;                   // 16-byte chunks per key row
     static constexpr int ROWB = D * 2;                  // bytes per key row
     static constexpr int TILEB = BK * ROWB;             // bytes per K (or V) tile
@@ -115,10 +116,13 @@ struct Cfg {
     static constexpr int ROWS_PER_KB = 1024 / ROWB;     // key rows per 1 KB wave load
     static constexpr int DS = D / 16;                   // k-steps of S = K Q^T
     static constexpr int DB = D / 32;                   // 32-row blocks of O^T
-    static constexpr int PART_ROWS = BK / LPT;          // key rows per LDS object (one per direct load)
+    static constexpr int PARTS = LPT >= 2 ? 2 : 1;      // LDS objects per K (or V) buffer
+    static constexpr int LPP = LPT / PARTS;             // direct loads per thread into each object
+    static constexpr int PART_ROWS = BK / PARTS;        // key rows per LDS object
     static constexpr int PARTB = PART_ROWS * ROWB;      // bytes per LDS object
     static_assert(LPT >= 1 && LPT * NT * 16 == TILEB, "tile must split into whole wave loads");
-    static_assert(PART_ROWS % 32 == 0, "a 32-key block must lie inside one LDS object");
+    static_assert(LPP * PARTS == LPT && PART_ROWS % 32 == 0, "a 32-key block must lie inside one LDS object");
+    static_assert(DS >= 2 * LPT, "the K and V loads of a tile are spread over the k-steps of [A]");
 };
 
 // 16-byte chunk swizzles (XOR with a per-row constant, so a bijection inside
@@ -128,10 +132,10 @@ struct Cfg {
 // go to different 64-byte bank groups; it depends on row % 8 only.  Because of
 // that, the per-lane part of every LDS address is fixed and all the rest
 // (k-step, key block, buffer) is a compile-time offset.
-template <int D>
-__device__ __forceinline__ int swz_k(int row) { return row & 15 & (Cfg<D>::CPR - 1); }
-template <int D>
-__device__ __forceinline__ int swz_v(int row) { return (((row & 3) << 2) | ((row >> 2) & 1)) & (Cfg<D>::CPR - 1); }
+template <int D, int NW>
+__device__ __forceinline__ int swz_k(int row) { return row & 15 & (Cfg<D, NW>::CPR - 1); }
+template <int D, int NW>
+__device__ __forceinline__ int swz_v(int row) { return (((row & 3) << 2) | ((row >> 2) & 1)) & (Cfg<D, NW>::CPR - 1); }
 
 template <int NS>
 struct Params {
@@ -215,41 +219,46 @@ __device__ __forceinline__ void advance(Cursor& cu, const Call& c, const TileRan
 // of a K (or V) tile, the key row inside the tile it fills and the byte offset
 // (from the tile's first key row of this head) of the swizzle-mapped source
 // chunk for K and for V.
-template <int D>
+template <int D, int NW>
 struct LoadMap {
-    int32_t row[Cfg<D>::LPT];
-    uint32_t kg[Cfg<D>::LPT];
-    uint32_t vg[Cfg<D>::LPT];
+    int32_t row[Cfg<D, NW>::LPT];
+    uint32_t kg[Cfg<D, NW>::LPT];
+    uint32_t vg[Cfg<D, NW>::LPT];
 };
 
-template <int D>
-__device__ __forceinline__ LoadMap<D> load_map(int wave, uint32_t row_bytes) {
-    using C = Cfg<D>;
+template <int D, int NW>
+__device__ __forceinline__ LoadMap<D, NW> load_map(int wave, uint32_t row_bytes) {
+    using C = Cfg<D, NW>;
     const int lane = threadIdx.x & 63;
-    LoadMap<D> m;
+    LoadMap<D, NW> m;
 #pragma unroll
     for (int i = 0; i < C::LPT; ++i) {
-        // load i of every wave fills LDS object (part) i; wave w fills its 1 KB block w
-        const int row = i * C::PART_ROWS + wave * C::ROWS_PER_KB + lane / C::CPR;  // key row in the tile
+        // load i of every wave fills 1 KB block (i % LPP) * NW + wave of LDS object i / LPP
+        const int row = (i / C::LPP) * C::PART_ROWS + ((i % C::LPP) * NW + wave) * C::ROWS_PER_KB +
+                        lane / C::CPR;  // key row in the tile
         const int phys = lane % C::CPR;                                           // chunk position it lands in
         m.row[i] = row;
-        m.kg[i] = (uint32_t)row * row_bytes + (uint32_t)((phys ^ swz_k<D>(row)) * 16);
-        m.vg[i] = (uint32_t)row * row_bytes + (uint32_t)((phys ^ swz_v<D>(row)) * 16);
+        m.kg[i] = (uint32_t)row * row_bytes + (uint32_t)((phys ^ swz_k<D, NW>(row)) * 16);
+        m.vg[i] = (uint32_t)row * row_bytes + (uint32_t)((phys ^ swz_v<D, NW>(row)) * 16);
     }
     return m;
 }
 
 // The LDS objects of one K or V buffer: part i holds key rows
 // [i * PART_ROWS, (i + 1) * PART_ROWS), each unpadded [row][dim].
-template <int D>
+template <int D, int NW>
 struct Buf {
-    char LDS_AS* part[Cfg<D>::LPT];
+    char LDS_AS* part[Cfg<D, NW>::PARTS];
+    // LDS block that direct load i of `wave` fills
+    __device__ __forceinline__ char LDS_AS* load_dst(int i, int wave) const {
+        return part[i / Cfg<D, NW>::LPP] + ((i % Cfg<D, NW>::LPP) * NW + wave) * 1024;
+    }
     // row kb * 32 + r (0 <= r < 32) of the tile: the object is known at compile
     // time from kb, so the compiler can keep the objects apart
     template <int KB>
     __device__ __forceinline__ char LDS_AS* block_row(int r) const {
-        constexpr int P = (KB * 32) / Cfg<D>::PART_ROWS, R0 = (KB * 32) % Cfg<D>::PART_ROWS;
-        return part[P] + (R0 + r) * Cfg<D>::ROWB;
+        constexpr int P = (KB * 32) / Cfg<D, NW>::PART_ROWS, R0 = (KB * 32) % Cfg<D, NW>::PART_ROWS;
+        return part[P] + (R0 + r) * Cfg<D, NW>::ROWB;
     }
 };
 
@@ -273,10 +282,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t off, ch
 // span end (or the last key) loads each span's rows under a lane mask; rows
 // past the last key read the last key instead (finite data that the mask
 // drops).
-template <int D, class Call>
-__device__ __forceinline__ void issue_tile(const Call& c, int32_t head, const Cursor& cu, const LoadMap<D>& m,
-                                           int wave, const Buf<D>& kbuf, const Buf<D>& vbuf, bool do_k, bool do_v) {
-    using C = Cfg<D>;
+template <int D, int NW, class Call>
+__device__ __forceinline__ void issue_tile(const Call& c, int32_t head, const Cursor& cu, const LoadMap<D, NW>& m,
+                                           int wave, const Buf<D, NW>& kbuf, const Buf<D, NW>& vbuf, bool do_k, bool do_v) {
+    using C = Cfg<D, NW>;
     const int64_t row_bytes = (int64_t)c.heads * D * 2;
     const uint32_t tile_bytes = (uint32_t)(BK * row_bytes);  // < 2^31: checked on the host
     if (cu.run > 0) {
@@ -284,8 +293,8 @@ __device__ __forceinline__ void issue_tile(const Call& c, int32_t head, const Cu
         const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(cu.v, tile_bytes);
 #pragma unroll
         for (int i = 0; i < C::LPT; ++i) {
-            if (do_k) dma16(rk, m.kg[i], kbuf.part[i] + wave * 1024);
-            if (do_v) dma16(rv, m.vg[i], vbuf.part[i] + wave * 1024);
+            if (do_k) dma16(rk, m.kg[i], kbuf.load_dst(i, wave));
+            if (do_v) dma16(rv, m.vg[i], vbuf.load_dst(i, wave));
         }
         return;
     }
@@ -307,8 +316,8 @@ __device__ __forceinline__ void issue_tile(const Call& c, int32_t head, const Cu
             if (j >= sb && j < se) {
                 // (j - r0) rows below the resource start, at this lane's chunk
                 const uint32_t off = (uint32_t)((j - r0) - m.row[i]) * (uint32_t)row_bytes;
-                if (do_k) dma16(rk, off + m.kg[i], kbuf.part[i] + wave * 1024);
-                if (do_v) dma16(rv, off + m.vg[i], vbuf.part[i] + wave * 1024);
+                if (do_k) dma16(rk, off + m.kg[i], kbuf.load_dst(i, wave));
+                if (do_v) dma16(rv, off + m.vg[i], vbuf.load_dst(i, wave));
             }
         }
     }
@@ -331,20 +340,20 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 // Per-lane LDS byte offsets (relative to an LDS object), fixed for the kernel.
-template <int D>
+template <int D, int NW>
 struct LdsAddr {
-    uint32_t k[Cfg<D>::DS];  // A operand of S^T, k-step ds: row l32, chunk (2 ds + h) ^ swz
-    uint32_t v[Cfg<D>::DB];  // V^T fragment of O block db (t = u = 0, block 0)
+    uint32_t k[Cfg<D, NW>::DS];  // A operand of S^T, k-step ds: row l32, chunk (2 ds + h) ^ swz
+    uint32_t v[Cfg<D, NW>::DB];  // V^T fragment of O block db (t = u = 0, block 0)
 };
 
-template <int D>
-__device__ __forceinline__ LdsAddr<D> lds_addr(int lane) {
-    using C = Cfg<D>;
-    LdsAddr<D> a;
+template <int D, int NW>
+__device__ __forceinline__ LdsAddr<D, NW> lds_addr(int lane) {
+    using C = Cfg<D, NW>;
+    LdsAddr<D, NW> a;
     const int l32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ++ds)
-        a.k[ds] = (uint32_t)(l32 * C::ROWB + (((2 * ds + h) ^ swz_k<D>(l32)) * 16));
+        a.k[ds] = (uint32_t)(l32 * C::ROWB + (((2 * ds + h) ^ swz_k<D, NW>(l32)) * 16));
     // transposing reads: in a 16-lane group, lane 4e+q names row 4h+e, dims 4q..4q+3
     // of its 16-dim half g&1 (g = lane/16, h = g/2)
     const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3, hh = g >> 1;
@@ -352,15 +361,15 @@ __device__ __forceinline__ LdsAddr<D> lds_addr(int lane) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
         const int d = db * 32 + 16 * (g & 1) + 4 * q;
-        a.v[db] = (uint32_t)(r * C::ROWB + (((d >> 3) ^ swz_v<D>(r)) * 16) + (d & 7) * 2);
+        a.v[db] = (uint32_t)(r * C::ROWB + (((d >> 3) ^ swz_v<D, NW>(r)) * 16) + (d & 7) * 2);
     }
     return a;
 }
 
 // S^T = K Q^T for one tile (two blocks of 32 keys), K from an LDS buffer.
-template <int D>
-__device__ __forceinline__ void qk_tile(const Buf<D>& kbuf, const bf16x8* qf, const LdsAddr<D>& la, f32x16* s) {
-    using C = Cfg<D>;
+template <int D, int NW>
+__device__ __forceinline__ void qk_tile(const Buf<D, NW>& kbuf, const bf16x8* qf, const LdsAddr<D, NW>& la, f32x16* s) {
+    using C = Cfg<D, NW>;
     s[0] = f32x16{};
     s[1] = f32x16{};
     const char LDS_AS* b0 = kbuf.template block_row<0>(0);
@@ -380,9 +389,9 @@ __device__ __forceinline__ void qk_tile(const Buf<D>& kbuf, const bf16x8* qf, co
 // lanes i/4, i/4+4, i/4+8, i/4+12, i.e. one dim (db*32 + lane%32) for 4 keys.
 // Two reads give the 8 keys of this lane's half: 16t + 8u + 4h + {0..3}, the
 // key order of the S^T accumulator registers 8t..8t+7.
-template <int D, int KB>
-__device__ __forceinline__ bf16x8 v_frag(const Buf<D>& vbuf, const LdsAddr<D>& la, int db, int t) {
-    using C = Cfg<D>;
+template <int D, int NW, int KB>
+__device__ __forceinline__ bf16x8 v_frag(const Buf<D, NW>& vbuf, const LdsAddr<D, NW>& la, int db, int t) {
+    using C = Cfg<D, NW>;
     const char LDS_AS* base = vbuf.template block_row<KB>(16 * t) + la.v[db];
     const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)base);
     const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 LDS_AS*)(base + 8 * C::ROWB));
@@ -440,8 +449,9 @@ __device__ __forceinline__ float load_f32_vmem(const float* ptr, bool ok) {
 // attention kernel (stream order makes the pieces visible: no fences, no
 // counters -- device-scope fences between pieces on different XCDs cost more
 // than the whole tail).
-template <int D>
+template <int D, int NW>
 struct SplitWs {
+    static constexpr int BQ = NW * 32;
     static constexpr size_t kO = (size_t)BQ * D;
     static __device__ __forceinline__ float* piece(void* ws, int32_t idx) {
         return (float*)ws + (size_t)idx * (kO + 2 * BQ);
@@ -451,9 +461,12 @@ struct SplitWs {
     }
 };
 
-template <int D, int NS, bool Q8>
-__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
-    using C = Cfg<D>;
+template <int D, int NS, bool Q8, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Params<NS> prm) {
+    using C = Cfg<D, NW>;
+    constexpr int BQ = C::BQ;
+    constexpr int kK8P = kTile8 / (NW * 1024);  // direct loads per thread of a K8 tile
+    static_assert(kK8P >= 1 && kK8P * NW * 1024 == kTile8, "a K8 tile splits into whole wave loads");
     static_assert(!Q8 || D == kD8, "FP8 QK^T is built for head_dim 128");
     static_assert(!Q8 || C::PARTB == kTile8, "a K8 tile fills the first LDS object of a K buffer");
     const AttnCallN<NS>& c = prm.c;
@@ -463,23 +476,23 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     // by direct loads from the ones being read -- and the direct loads of one
     // tile from each other -- and adds no waits between them.
     __shared__ __attribute__((aligned(1024))) char k0p0[C::PARTB];
-    __shared__ __attribute__((aligned(1024))) char k0p1[C::LPT > 1 && !Q8 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char k0p1[C::PARTS > 1 && !Q8 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char k1p0[C::PARTB];
-    __shared__ __attribute__((aligned(1024))) char k1p1[C::LPT > 1 && !Q8 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char k1p1[C::PARTS > 1 && !Q8 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char v0p0[C::PARTB];
-    __shared__ __attribute__((aligned(1024))) char v0p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char v0p1[C::PARTS > 1 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char v1p0[C::PARTB];
-    __shared__ __attribute__((aligned(1024))) char v1p1[C::LPT > 1 ? C::PARTB : 16];
+    __shared__ __attribute__((aligned(1024))) char v1p1[C::PARTS > 1 ? C::PARTB : 16];
     __shared__ __attribute__((aligned(1024))) char dummy[NW * 1024];  // sink of loads that fetch nothing
-    static_assert(C::LPT <= 2, "at most two LDS objects per buffer");
+    static_assert(C::PARTS <= 2, "at most two LDS objects per buffer");
     auto mkbuf = [](char* p0, char* p1) {
-        Buf<D> b;
+        Buf<D, NW> b;
         b.part[0] = (char LDS_AS*)p0;
-        if constexpr (C::LPT > 1) b.part[C::LPT - 1] = (char LDS_AS*)p1;
+        if constexpr (C::PARTS > 1) b.part[C::PARTS - 1] = (char LDS_AS*)p1;
         return b;
     };
-    const Buf<D> kb0 = mkbuf(k0p0, k0p1), kb1 = mkbuf(k1p0, k1p1);
-    const Buf<D> vb0 = mkbuf(v0p0, v0p1), vb1 = mkbuf(v1p0, v1p1);
+    const Buf<D, NW> kb0 = mkbuf(k0p0, k0p1), kb1 = mkbuf(k1p0, k1p1);
+    const Buf<D, NW> vb0 = mkbuf(v0p0, v0p1), vb1 = mkbuf(v1p0, v1p1);
 
     // ---- which unit (head, q-tile) and which key-tile range this workgroup runs
     [[maybe_unused]] uint64_t pc_entry = 0;
@@ -607,8 +620,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         const float sk = p.k8_scale[(size_t)tile * c.heads + head];
         return sk > 0.0f ? sk : 1.0f;  // an all-zero tile has zero codes: any positive factor
     };
-    const LoadMap<D> lm = load_map<D>(wave, (uint32_t)(c.heads * D * 2));
-    const LdsAddr<D> la = lds_addr<D>(lane);
+    const LoadMap<D, NW> lm = load_map<D, NW>(wave, (uint32_t)(c.heads * D * 2));
+    const LdsAddr<D, NW> la = lds_addr<D, NW>(lane);
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -700,19 +713,25 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
     WMK_STAMP(fl1);
     if (it0 < it1) {
         if constexpr (Q8) {
-            dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane, kb0.part[0] + wave * 1024);
-            issue_tile<D>(c, head, vcu, lm, wave, kb0, vb0, false, true);
+#pragma unroll
+            for (int j = 0; j < kK8P; ++j)
+                dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane + j * NW * 1024,
+                      kb0.part[0] + (j * NW + wave) * 1024);
+            issue_tile<D, NW>(c, head, vcu, lm, wave, kb0, vb0, false, true);
             cs_a = cs0 * k8_scale(vcu.tile);
         } else {
-            issue_tile<D>(c, head, vcu, lm, wave, kb0, vb0, true, true);
+            issue_tile<D, NW>(c, head, vcu, lm, wave, kb0, vb0, true, true);
         }
         advance(vcu, c, tr, it0 + 1, row_bytes, head_off);
         if (it0 + 1 < it1) {
             if constexpr (Q8) {
-                dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane, kb1.part[0] + wave * 1024);
+#pragma unroll
+                for (int j = 0; j < kK8P; ++j)
+                    dma16(buffer_rsrc(k8_src(vcu.tile), kTile8), k8_lane + j * NW * 1024,
+                          kb1.part[0] + (j * NW + wave) * 1024);
                 cs_b = cs0 * k8_scale(vcu.tile);
             } else {
-                issue_tile<D>(c, head, vcu, lm, wave, kb1, vb1, true, false);
+                issue_tile<D, NW>(c, head, vcu, lm, wave, kb1, vb1, true, false);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -721,7 +740,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         WMK_STAMP(fl3);
         if (wave_has_rows) {
             if constexpr (Q8) qk_tile8(kb0.part[0], qf8, k8o, s);
-            else qk_tile<D>(kb0, qf, la, s);
+            else qk_tile<D, NW>(kb0, qf, la, s);
             mask_tile(tile0);
             new_ref();  // O and l are still zero
             const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
@@ -747,10 +766,10 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         WMK_STAMP(pc_s);
         constexpr int ST = decltype(st_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
-        const Buf<D>& kcur = ST ? kb1 : kb0;
-        const Buf<D>& knext = ST ? kb0 : kb1;
-        const Buf<D>& vcur = ST ? vb1 : vb0;
-        const Buf<D>& vnext = ST ? vb0 : vb1;
+        const Buf<D, NW>& kcur = ST ? kb1 : kb0;
+        const Buf<D, NW>& knext = ST ? kb0 : kb1;
+        const Buf<D, NW>& vcur = ST ? vb1 : vb0;
+        const Buf<D, NW>& vnext = ST ? vb0 : vb1;
         // K(it+2) into kcur and V(it+1) into vnext, both read last in the
         // previous step; spread over the MFMAs of [A] (the tile interface is
         // busy for a while with each direct load, and a wave that issues all of
@@ -760,9 +779,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         const bool k_ok = it + 2 < it1, v_ok = it + 1 < it1;
         const bool k_fast = k_ok && (Q8 || kcu.run > 0), v_fast = v_ok && vcu.run > 0;
         if constexpr (!Q8) {
-            if (k_ok && !k_fast) issue_tile<D>(c, head, kcu, lm, wave, kcur, vnext, true, false);
+            if (k_ok && !k_fast) issue_tile<D, NW>(c, head, kcu, lm, wave, kcur, vnext, true, false);
         }
-        if (v_ok && !v_fast) issue_tile<D>(c, head, vcu, lm, wave, kcur, vnext, false, true);
+        if (v_ok && !v_fast) issue_tile<D, NW>(c, head, vcu, lm, wave, kcur, vnext, false, true);
         const __amdgpu_buffer_rsrc_t krs =
             Q8 ? buffer_rsrc(k8_src(k_ok ? kcu.tile : 0), k_ok ? (uint32_t)kTile8 : 0u)
                : buffer_rsrc(kcu.k, k_fast ? tile_bytes : 0u);
@@ -772,11 +791,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         if constexpr (Q8 && !LAST)
             sk_next = load_f32_vmem(p.k8_scale + (size_t)(k_ok ? kcu.tile : 0) * c.heads + head, k_ok);
         auto k_piece = [&](int i) __attribute__((always_inline)) {
-            if constexpr (Q8) dma16(krs, k8_lane, (k_ok ? kcur.part[0] : (char LDS_AS*)dummy) + wave * 1024);
-            else dma16(krs, lm.kg[i], (k_fast ? kcur.part[i] : (char LDS_AS*)dummy) + wave * 1024);
+            if constexpr (Q8)
+                dma16(krs, k8_lane + i * NW * 1024,
+                      k_ok ? kcur.part[0] + (i * NW + wave) * 1024 : (char LDS_AS*)dummy + wave * 1024);
+            else dma16(krs, lm.kg[i], k_fast ? kcur.load_dst(i, wave) : (char LDS_AS*)dummy + wave * 1024);
         };
         auto v_piece = [&](int i) __attribute__((always_inline)) {
-            dma16(vrs, lm.vg[i], (v_fast ? vnext.part[i] : (char LDS_AS*)dummy) + wave * 1024);
+            dma16(vrs, lm.vg[i], v_fast ? vnext.load_dst(i, wave) : (char LDS_AS*)dummy + wave * 1024);
         };
         const int32_t tile_next = vcu.tile;
         vcu = kcu;
@@ -784,7 +805,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
         if (!wave_has_rows && !LAST) {
 #pragma unroll
             for (int i = 0; i < C::LPT; ++i) {
-                if (!Q8 || i == 0) k_piece(i);
+                if (!Q8 || i < kK8P) k_piece(i);
                 v_piece(i);
             }
         }
@@ -819,7 +840,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 #pragma unroll
                 for (int ks = 0; ks < kDS8; ++ks) {
                     sn0 = mfma8(ka8[ks][0], qf8[ks], sn0);
-                    if (ks == 0) k_piece(0);
+#pragma unroll
+                    for (int j = 0; j < kK8P; ++j)
+                        if (j % kDS8 == ks) k_piece(j);
 #pragma unroll
                     for (int i = 0; i < C::LPT; ++i)
                         if (i * kDS8 / C::LPT == ks) v_piece(i);
@@ -849,8 +872,11 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
                         ka[(ds + KPF) % (KPF + 1)][1] = *(const bf16x8 LDS_AS*)(kn1 + la.k[ds + KPF]);
                     }
                     sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ds % (KPF + 1)][0], qf[ds], sn0, 0, 0, 0);
-                    if (ds % 4 == 1 && ds / 4 < C::LPT) k_piece(ds / 4);  // K pieces at ds 1, 5; V at 3, 7
-                    if (ds % 4 == 3 && ds / 4 < C::LPT) v_piece(ds / 4);
+                    // the LPT K pieces and LPT V pieces, alternating, one per SP / 2 k-steps
+                    // (8 waves, head_dim 128: K at ds 1, 5; V at 3, 7)
+                    constexpr int SP = C::DS / C::LPT;
+                    if (ds % SP == SP / 4) k_piece(ds / SP);
+                    if (ds % SP == (3 * SP) / 4) v_piece(ds / SP);
 #pragma unroll
                     for (int x = 0; x < EPS; ++x) {
                         const int idx = ds * EPS + x;
@@ -903,8 +929,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             constexpr int WSLOTS = NPV - 1 - WFIRST;
             auto vfrag_at = [&](auto i_c) __attribute__((always_inline)) -> bf16x8 {
                 constexpr int i = decltype(i_c)::value;
-                if constexpr (i % 2 == 0) return v_frag<D, 0>(vcur, la, i / 4, (i / 2) % 2);
-                else return v_frag<D, 1>(vcur, la, i / 4, (i / 2) % 2);
+                if constexpr (i % 2 == 0) return v_frag<D, NW, 0>(vcur, la, i / 4, (i / 2) % 2);
+                else return v_frag<D, NW, 1>(vcur, la, i / 4, (i / 2) % 2);
             };
             bf16x8 vfr[VPF + 1];
             [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
@@ -1011,7 +1037,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 
 #ifdef WMK_STEP_PROFILE
     if (lane == 0 && blockIdx.x < 4096) {
-        unsigned long long* e = g_step_prof[blockIdx.x * NW + wave];
+        unsigned long long* e = g_step_prof[blockIdx.x * 8 + wave];  // 8 records per workgroup
         for (int i = 0; i < 7; ++i) e[i] = prof[i];
         e[7] = (unsigned long long)head << 32 | (unsigned long long)qt << 8 | (unsigned long long)(piece < 0 ? 255 : piece);
         e[8] = real_last - real_first;
@@ -1047,7 +1073,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
 
     // ---- split tail: publish this piece; attn_merge_kernel combines the pieces
     const int32_t su = u - full_units;
-    float* w = SplitWs<D>::piece(p.ws, su * p.splits + piece);
+    float* w = SplitWs<D, NW>::piece(p.ws, su * p.splits + piece);
     const int rl = wave * 32 + l32;  // row within the tile
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -1056,8 +1082,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Params<NS> prm) {
             *(f32x4*)(w + (size_t)rl * D + db * 32 + 8 * g + 4 * h) =
                 f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
     if (h == 0) {
-        w[SplitWs<D>::kO + 2 * rl] = m_ref;
-        w[SplitWs<D>::kO + 2 * rl + 1] = l_tot;
+        w[SplitWs<D, NW>::kO + 2 * rl] = m_ref;
+        w[SplitWs<D, NW>::kO + 2 * rl + 1] = l_tot;
     }
 }
 
@@ -1075,8 +1101,9 @@ struct MergeArgs {
     int32_t splits;
 };
 
-template <int D>
+template <int D, int NW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
+    constexpr int BQ = NW * 32;
     constexpr int TPR = D / 8;  // threads per row
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (gid >= (int64_t)a.split_units * BQ * TPR) return;
@@ -1088,14 +1115,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
     if (row >= a.q_tokens) return;
     float mmax = -INFINITY;
     for (int q = 0; q < a.splits; ++q)
-        mmax = fmaxf(mmax, SplitWs<D>::piece(a.ws, su * a.splits + q)[SplitWs<D>::kO + 2 * rl]);
+        mmax = fmaxf(mmax, SplitWs<D, NW>::piece(a.ws, su * a.splits + q)[SplitWs<D, NW>::kO + 2 * rl]);
     const float mref = (mmax == -INFINITY) ? 0.0f : mmax;
     f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
     float lt = 0.0f;
     for (int q = 0; q < a.splits; ++q) {
-        const float* w = SplitWs<D>::piece(a.ws, su * a.splits + q);
-        const float wq = __builtin_amdgcn_exp2f(w[SplitWs<D>::kO + 2 * rl] - mref);
-        lt += wq * w[SplitWs<D>::kO + 2 * rl + 1];
+        const float* w = SplitWs<D, NW>::piece(a.ws, su * a.splits + q);
+        const float wq = __builtin_amdgcn_exp2f(w[SplitWs<D, NW>::kO + 2 * rl] - mref);
+        lt += wq * w[SplitWs<D, NW>::kO + 2 * rl + 1];
         const f32x4* src = (const f32x4*)(w + (size_t)rl * D + part * 8);
         acc0 += wq * src[0];
         acc1 += wq * src[1];
@@ -1110,20 +1137,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-int attn_bf16_block_q() { return BQ; }
+int attn_bf16_block_q(int waves) { return waves * 32; }
 
-size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t splits) {
+size_t attn_bf16_split_ws_bytes(int head_dim, int waves, int32_t split_units, int32_t splits) {
     if (split_units <= 0 || splits <= 0) return 0;
-    return (size_t)split_units * splits * ((size_t)BQ * head_dim + 2 * BQ) * sizeof(float);
+    const size_t bq = (size_t)waves * 32;
+    return (size_t)split_units * splits * (bq * head_dim + 2 * bq) * sizeof(float);
 }
 
-int attn_bf16_blocks_per_cu(int head_dim) {
+int attn_bf16_blocks_per_cu(int head_dim, int waves) {
     int n = 0;
     hipError_t e;
-    if (head_dim == 64)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kFewSeg, false>, NT, 0);
+    if (waves == kWavesShort)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, kFewSeg, false, kWavesShort>,
+                                                         kWavesShort * 64, 0);
+    else if (head_dim == 64)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<64, kFewSeg, false, kWavesLong>,
+                                                         kWavesLong * 64, 0);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, kFewSeg, false>, NT, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<128, kFewSeg, false, kWavesLong>,
+                                                         kWavesLong * 64, 0);
     return (e == hipSuccess && n > 0) ? n : 1;
 }
 
@@ -1147,12 +1180,15 @@ hipError_t launch_spans(const AttnCall& c, const AttnPlan& plan, int32_t blocks,
     }
     prm.c.kv.n = c.kv.n;
     prm.p = plan;
-    if (plan.k8 != nullptr)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, true>), dim3(blocks), dim3(NT), 0, s, prm);
+    constexpr int L = kWavesLong, S = kWavesShort;
+    if (plan.waves == S)  // bf16, head_dim 128 only (checked by the caller)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, false, S>), dim3(blocks), dim3(S * 64), 0, s, prm);
+    else if (plan.k8 != nullptr)
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, true, L>), dim3(blocks), dim3(L * 64), 0, s, prm);
     else if (c.head_dim == 64)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, NS, false>), dim3(blocks), dim3(NT), 0, s, prm);
+        hipLaunchKernelGGL((attn_bf16_kernel<64, NS, false, L>), dim3(blocks), dim3(L * 64), 0, s, prm);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, false>), dim3(blocks), dim3(NT), 0, s, prm);
+        hipLaunchKernelGGL((attn_bf16_kernel<128, NS, false, L>), dim3(blocks), dim3(L * 64), 0, s, prm);
     return hipGetLastError();
 }
 
@@ -1160,6 +1196,8 @@ hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t
     const int32_t blocks = plan.n_units - plan.split_units + plan.split_units * plan.splits;
     if (blocks <= 0) return hipSuccess;
     if (c.kv.n < 0 || c.kv.n > kMaxSeg || (c.head_dim != 64 && c.head_dim != 128)) return hipErrorInvalidValue;
+    if (plan.waves != kWavesLong && (plan.waves != kWavesShort || c.head_dim != 128 || plan.k8 != nullptr))
+        return hipErrorInvalidValue;
     if (plan.k8 != nullptr && (c.head_dim != 128 || plan.q8 == nullptr || plan.k8_scale == nullptr ||
                                plan.q8_scale == nullptr))
         return hipErrorInvalidValue;
@@ -1178,12 +1216,14 @@ hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t
     m.full_units = plan.n_units - plan.split_units;
     m.split_units = plan.split_units;
     m.splits = plan.splits;
-    const int64_t threads = (int64_t)plan.split_units * BQ * (c.head_dim / 8);
+    const int64_t threads = (int64_t)plan.split_units * plan.waves * 32 * (c.head_dim / 8);
     const dim3 grid((uint32_t)((threads + 255) / 256));
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(256), 0, s, m);
+    if (plan.waves == kWavesShort)
+        hipLaunchKernelGGL((attn_merge_kernel<128, kWavesShort>), grid, dim3(256), 0, s, m);
+    else if (c.head_dim == 64)
+        hipLaunchKernelGGL((attn_merge_kernel<64, kWavesLong>), grid, dim3(256), 0, s, m);
     else
-        hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(256), 0, s, m);
+        hipLaunchKernelGGL((attn_merge_kernel<128, kWavesLong>), grid, dim3(256), 0, s, m);
     return hipGetLastError();
 }
 

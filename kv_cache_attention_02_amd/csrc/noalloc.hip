@@ -23,8 +23,10 @@
 namespace wmk {
 namespace {
 
-// 256 split pieces -- one per resident workgroup of the attention kernel on a
-// 256-CU MI355X -- of 256 query rows x 128 dims in fp32, plus (max, sum) per row.
+// 256 split pieces -- one per resident workgroup of the 8-wave attention kernel
+// on a 256-CU MI355X -- of 256 query rows x 128 dims in fp32, plus (max, sum)
+// per row; the same bytes hold the 512 pieces of 128 rows of the 4-wave kernel
+// (two workgroups per CU).
 constexpr size_t kScratchBytes = (size_t)256 * (256 * 128 + 2 * 256) * sizeof(float);
 constexpr int kMaxDevices = 64;
 

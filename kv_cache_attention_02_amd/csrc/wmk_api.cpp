@@ -124,17 +124,21 @@ int64_t valid_of(const wmk_cache_desc& d, int64_t F) {
 // ---- per-device facts used by the planner
 struct DeviceInfo {
     int cus = 0;
-    int bpc64 = 0, bpc128 = 0;
+    int bpc64 = 0, bpc128 = 0, bpc128_short = 0;  // resident workgroups per CU of the bf16 kernels
+    int slots(int head_dim, int waves) const {
+        return cus * (waves == wmk::kWavesShort ? bpc128_short : head_dim == 64 ? bpc64 : bpc128);
+    }
 };
 std::mutex g_dev_mu;
 std::vector<DeviceInfo> g_dev;
 
 DeviceInfo device_info() {
-    if (dry_run_path() != nullptr) {  // no device: an MI355X-like 256 CUs, one workgroup each
+    if (dry_run_path() != nullptr) {  // no device: an MI355X-like 256 CUs, one 8-wave or two 4-wave workgroups each
         DeviceInfo di;
         di.cus = 256;
         di.bpc64 = 1;
         di.bpc128 = 1;
+        di.bpc128_short = 2;
         return di;
     }
     int dev = 0;
@@ -147,8 +151,9 @@ DeviceInfo device_info() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
             cus = 256;
         di.cus = cus;
-        di.bpc64 = wmk::attn_bf16_blocks_per_cu(64);
-        di.bpc128 = wmk::attn_bf16_blocks_per_cu(128);
+        di.bpc64 = wmk::attn_bf16_blocks_per_cu(64, wmk::kWavesLong);
+        di.bpc128 = wmk::attn_bf16_blocks_per_cu(128, wmk::kWavesLong);
+        di.bpc128_short = wmk::attn_bf16_blocks_per_cu(128, wmk::kWavesShort);
     }
     return di;
 }
@@ -167,15 +172,14 @@ size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, int32_
     p.splits = 1;
     p.ws = nullptr;
     if (tiles_per_unit < 2 * kMinTilesPerPiece) return 0;
-    const DeviceInfo di = device_info();
-    const int slots = di.cus * (head_dim == 64 ? di.bpc64 : di.bpc128);
+    const int slots = device_info().slots(head_dim, p.waves);
     if (slots <= 0) return 0;
     const int32_t rounds = p.n_units / slots, tail = p.n_units % slots;
     if (rounds < 1 || tail == 0) return 0;
     int32_t splits = std::min<int32_t>(slots / tail, tiles_per_unit / kMinTilesPerPiece);
     splits = std::min<int32_t>(splits, INT32_MAX / std::max(kv_tiles, 1));
     if (splits < 2) return 0;
-    const size_t need = wmk::attn_bf16_split_ws_bytes(head_dim, tail, splits);
+    const size_t need = wmk::attn_bf16_split_ws_bytes(head_dim, p.waves, tail, splits);
     // (the pieces store 16-byte vectors: a misaligned workspace is not used)
     if (ws == nullptr || ((uintptr_t)ws & 15) != 0 || need > ws_bytes) return need;
     p.split_units = tail;
@@ -186,7 +190,7 @@ size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, int32_
 
 // Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
 int32_t moba_qtile_cost(const wmk::MaskShape& m, int32_t q_tokens, int32_t qt) {
-    const int32_t bq = wmk::attn_bf16_block_q();
+    const int32_t bq = wmk::attn_bf16_block_q(wmk::kWavesLong);  // MoBA runs the 8-wave kernel
     const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, q_tokens);
     const int32_t L = m.part_len, cl = m.chunk_len;
     std::vector<std::pair<int32_t, int32_t>> iv;
@@ -267,7 +271,18 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
     } else {
         wmk::AttnPlan p;
         memset(&p, 0, sizeof p);
-        const int32_t bq = wmk::attn_bf16_block_q();
+        // every q-tile of a chunk-attention or cross-mask call visits the same
+        // number of key tiles: the whole key range, or (cross mask) the
+        // environment prompt plus its chunks' local prompts
+        const int32_t kv_tiles = (int32_t)(((int64_t)call.kv_total + kBK - 1) / kBK);
+        int32_t tiles = kv_tiles;
+        if (call.mask.mode == wmk::kMaskCross)
+            tiles = (call.mask.env_len + kBK - 1) / kBK + (call.mask.chunk_len + kBK - 1) / kBK;
+        p.waves = wmk::kWavesLong;
+        if (call.mask.mode != wmk::kMaskMoba && call.head_dim == 128 && qk8 == nullptr &&
+            tiles <= wmk::kShortUnitTiles)
+            p.waves = wmk::kWavesShort;
+        const int32_t bq = wmk::attn_bf16_block_q(p.waves);
         p.n_qtiles = (call.q_tokens + bq - 1) / bq;
         p.n_units = p.n_qtiles * call.heads;
         p.splits = 1;
@@ -275,13 +290,6 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
             plan_moba_groups(p, call.mask, call.q_tokens);
             p.xcd_remap = 0;
         } else {
-            // every q-tile visits the same number of key tiles: the whole key
-            // range, or (cross mask) the environment prompt plus its chunks'
-            // local prompts
-            const int32_t kv_tiles = (int32_t)(((int64_t)call.kv_total + kBK - 1) / kBK);
-            int32_t tiles = kv_tiles;
-            if (call.mask.mode == wmk::kMaskCross)
-                tiles = (call.mask.env_len + kBK - 1) / kBK + (call.mask.chunk_len + kBK - 1) / kBK;
             p.xcd_remap = 1;
             const size_t need = plan_split(p, call.head_dim, tiles, kv_tiles, ws, ws_bytes);
             if (strict_ws && need > ws_bytes)
@@ -617,12 +625,19 @@ wmk_status wmk_cache_slots(const wmk_cache* c, int32_t layer, int64_t* frame_of_
 size_t wmk_attention_workspace_bytes(const wmk_head_desc* hd, int32_t q_tokens) {
     if (check_head(hd) != WMK_OK || q_tokens <= 0 || hd->dtype != WMK_BF16) return 0;
     const DeviceInfo di = device_info();
-    const int slots = di.cus * (hd->head_dim == 64 ? di.bpc64 : di.bpc128);
-    const int32_t bq = wmk::attn_bf16_block_q();
-    const int64_t units = (int64_t)((q_tokens + bq - 1) / bq) * hd->num_heads;
-    const int32_t tail = (int32_t)std::min<int64_t>(units, slots);
-    // pieces never exceed the number of resident workgroups
-    return wmk::attn_bf16_split_ws_bytes(hd->head_dim, tail, std::max(1, slots / std::max(1, tail)));
+    // the larger need of the two kernel shapes a call may get (pieces never
+    // exceed the number of resident workgroups)
+    size_t need = 0;
+    for (const int waves : {wmk::kWavesLong, wmk::kWavesShort}) {
+        if (waves == wmk::kWavesShort && hd->head_dim != 128) continue;
+        const int slots = di.slots(hd->head_dim, waves);
+        const int32_t bq = wmk::attn_bf16_block_q(waves);
+        const int64_t units = (int64_t)((q_tokens + bq - 1) / bq) * hd->num_heads;
+        const int32_t tail = (int32_t)std::min<int64_t>(units, slots);
+        need = std::max(need, wmk::attn_bf16_split_ws_bytes(hd->head_dim, waves, tail,
+                                                            std::max(1, slots / std::max(1, tail))));
+    }
+    return need;
 }
 
 wmk_status wmk_chunk_attention(const wmk_cache* c, int32_t layer, const wmk_head_desc* hd, const void* q,

@@ -75,8 +75,17 @@ using AttnCall = AttnCallN<kMaxSeg>;
 
 // Work plan for the bf16 MFMA kernel: which (head, q-tile) units run in which
 // launch order, and how the last partial round is split over the key range.
+// Waves per workgroup of the bf16 kernel: 8 (one workgroup per CU) for the
+// long key walks; 4 (two workgroups per CU, so that one's unit fill runs beside
+// the other's steps) for calls whose units walk at most kShortUnitTiles key
+// tiles -- bf16, head_dim 128.
+constexpr int kWavesLong = 8;
+constexpr int kWavesShort = 4;
+constexpr int kShortUnitTiles = 32;
+
 struct AttnPlan {
-    int32_t n_qtiles;       // ceil(q_tokens / attn_bf16_block_q())
+    int32_t waves;          // kWavesLong or kWavesShort
+    int32_t n_qtiles;       // ceil(q_tokens / attn_bf16_block_q(waves))
     int32_t n_units;        // n_qtiles * heads
     int32_t n_groups;       // > 0: q-tiles visited in this group order (longest first, grp_* below)
     int32_t xcd_remap;      // 1: keep consecutive units of one head on one XCD
@@ -105,14 +114,14 @@ struct AttnPlan {
 // bf16 MFMA attention.  Returns the launch status.
 hipError_t launch_attn_bf16(const AttnCall& c, const AttnPlan& plan, hipStream_t s);
 
-// Query rows per workgroup (q-tile) of the bf16 kernel.
-int attn_bf16_block_q();
+// Query rows per workgroup (q-tile) of the bf16 kernel with `waves` waves.
+int attn_bf16_block_q(int waves);
 
-// Number of resident workgroups of the bf16 kernel per CU (occupancy) for head_dim.
-int attn_bf16_blocks_per_cu(int head_dim);
+// Number of resident workgroups of the bf16 kernel per CU (occupancy) for head_dim and waves.
+int attn_bf16_blocks_per_cu(int head_dim, int waves);
 
-// Workspace bytes the bf16 kernel's split tail needs for `pieces` pieces.
-size_t attn_bf16_split_ws_bytes(int head_dim, int32_t split_units, int32_t splits);
+// Workspace bytes the bf16 kernel's split tail needs for split_units x splits pieces.
+size_t attn_bf16_split_ws_bytes(int head_dim, int waves, int32_t split_units, int32_t splits);
 
 // FP8 e4m3 block quantization of a bf16 [tokens][heads][head_dim] sequence
 // given as n_spans spans (end: exclusive prefix sums of their lengths) into

@@ -256,6 +256,45 @@ def test_plan_of_the_18_slot_step(lib, dry):
     lib.wmk_cache_destroy(h2)
 
 
+def test_short_units_plan_the_four_wave_kernel(lib, dry):
+    """Calls whose units walk at most 32 key tiles (bf16, head_dim 128, no MoBA mask) are
+    planned for the 4-wave kernel (128-row q-tiles, two workgroups per CU); longer walks,
+    head_dim 64 and the MoBA mask keep the 8-wave kernel (256-row q-tiles). The workspace
+    query covers both shapes."""
+    hd = wmk.wmk_head_desc(24, 128, wmk.WMK_BF16)
+    # 720p cross-attention: 14400 queries over a 512-token environment + a 512-token local prompt
+    segs = [(KBUF, VBUF, 512), (QBUF, SBUF, 512)]
+    assert _attn(lib, None, 0, hd, 14400, segs) == wmk.WMK_OK
+    p = _last_attn(dry)
+    assert (p["bq"], p["qtiles"], p["units"]) == ("128", str(-(-14400 // 128)), str(24 * -(-14400 // 128)))
+    # 32 tiles (2048 keys): still short; 33 tiles: long
+    assert _attn(lib, None, 0, hd, 14400, [(KBUF, VBUF, 2048)]) == wmk.WMK_OK
+    assert _last_attn(dry)["bq"] == "128"
+    assert _attn(lib, None, 0, hd, 14400, [(KBUF, VBUF, 2049)]) == wmk.WMK_OK
+    assert _last_attn(dry)["bq"] == "256"
+    # head_dim 64 keeps the 8-wave kernel
+    hd64 = wmk.wmk_head_desc(24, 64, wmk.WMK_BF16)
+    assert _attn(lib, None, 0, hd64, 14400, segs) == wmk.WMK_OK
+    assert _last_attn(dry)["bq"] == "256"
+    # the cross-attention training mask: 512 + 512 keys per row
+    xd = wmk.wmk_xattn_desc(4680, 7, 512, 512)
+    hd12 = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
+    assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd12), QBUF, KBUF, VBUF, OBUF, 0.088, None,
+                                         0, None) == wmk.WMK_OK
+    assert _last_attn(dry)["bq"] == "128"
+    # MoBA keeps the 8-wave kernel whatever its tile counts
+    md = wmk.wmk_moba_desc(40, 3, 1, 1)
+    assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd12), QBUF, KBUF, VBUF, OBUF, 0.088, None) == \
+        wmk.WMK_OK
+    assert _last_attn(dry)["bq"] == "256"
+    # one workspace size serves both shapes: with it the short call splits its tail
+    wsb = lib.wmk_attention_workspace_bytes(ctypes.byref(hd), 14400)
+    assert _attn(lib, None, 0, hd, 14400, segs, ws=0x60000000, wsb=wsb) == wmk.WMK_OK
+    p = _last_attn(dry)
+    units = 24 * -(-14400 // 128)  # 2712 units over 512 slots (two 4-wave workgroups per CU): 152 left over
+    assert p["bq"] == "128" and int(p["split_units"]) == units % 512 and int(p["splits"]) == min(512 // 152, 16 // 8)
+
+
 def _oracle_qtile_cost(qt, tpf, frames, cf, bq, bk=64):
     n = 3 * frames * tpf
     tiles = set()
@@ -340,9 +379,10 @@ def test_cross_train_argument_errors_and_plan(lib, dry):
     assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.088,
                                          0x60000000, wsb, None) == wmk.WMK_OK
     p = _last_attn(dry)
-    tail = (24 * qtiles) % 256
+    slots = 256 * (2 if bq == 128 else 1)  # dry-run device: one 8-wave or two 4-wave workgroups per CU
+    tail = (24 * qtiles) % slots
     # 8 + 8 key tiles per q-tile: exactly two pieces of the minimum size
-    assert int(p["split_units"]) == tail and int(p["splits"]) == min(256 // tail, 16 // 8)
+    assert int(p["split_units"]) == tail and int(p["splits"]) == min(slots // tail, 16 // 8)
 
 
 def _attn_keep(lib, h, layer, keep, hd, nq, segs, scale=0.088, keep_null=False):
