@@ -127,7 +127,8 @@ def step_profile(wmk, synth, torch, np, fill, stream, flops, workload="832x464")
     second-half weights), [B] (P V beside the next tile's row max and first-half weights),
     the wait for the step's own direct loads, the barrier, and the issue code before [A] --
     averaged per step, over the full units and over the split tail's pieces; waves 0-3 and
-    4-7 (the two waves of each SIMD) separately; the unit's fill (entry to the first step);
+    4-7 (the two waves of each SIMD of an 8-wave workgroup) separately (a call of short key
+    walks runs the 4-wave shape, whose records 4-7 stay empty); the unit's fill (entry to the first step);
     and the shader clock from the same span on the 100 MHz real-time counter.
     workload: the 832x464 step, or the 720p chunk's cross-attention."""
     import ctypes

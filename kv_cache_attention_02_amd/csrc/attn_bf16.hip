@@ -3,8 +3,10 @@
 // One workgroup = 8 waves = 256 query rows of one head (32 rows per wave); keys
 // are visited in tiles of 64.  K and V tiles go from global memory straight
 // into LDS (16-byte buffer loads with the LDS-destination form, no staging
-// registers) and are shared by the 8 waves; two K and two V buffers, one
-// barrier per tile.
+// registers) and are shared by the waves; two K and two V buffers, one
+// barrier per tile.  Calls whose units walk few key tiles run the same code
+// with 4 waves (128 rows) per workgroup and two workgroups per CU, so that one
+// workgroup's unit fill overlaps the other's steps.
 //
 // Per wave, iteration j (software pipelined across tiles):
 //   softmax of tile j            fp32, log2 domain: exp2 with scale*log2(e)
@@ -35,7 +37,7 @@
 // the workgroup allows are never visited: the workgroup walks only the union of
 // its rows' ranges, in tile units.
 //
-// Split tail: when there are too few units (256-row query tiles of one head)
+// Split tail: when there are too few units (query tiles of one head)
 // to fill the chip, the last units are cut into pieces along their key tiles.
 // Each piece writes its unnormalized O and per-row (max, sum) to a workspace;
 // attn_merge_kernel, launched after it on the same stream, combines the pieces
