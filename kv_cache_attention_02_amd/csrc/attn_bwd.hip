@@ -217,6 +217,10 @@ struct BwdArgs {
     int32_t heads;
     float scale;
     MaskShape mask;
+    // launch order of this kernel's tiles, longest walk first (0 groups: natural order)
+    int32_t n_groups;
+    int32_t grp_start[kMaxGroups];
+    int32_t grp_count[kMaxGroups];
 };
 
 // exp2 exponent offset of a row: lse in log2 units; a row with no key (lse =
@@ -247,8 +251,23 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(const __bf16* dout, const
     }
 }
 
-// workgroup -> (head, tile of BR rows); consecutive tiles of one head share an XCD
-__device__ __forceinline__ void unit_of(int32_t b, int32_t units, int32_t n_tiles, int32_t& head, int32_t& t) {
+// workgroup -> (head, tile of BR rows or keys).  With a group table: the
+// tiles longest walk first, all heads of a tile together (a uniform walk length
+// per launch position keeps the last round short); without: consecutive tiles
+// of one head share an XCD.
+__device__ __forceinline__ void unit_of(const BwdArgs& a, int32_t b, int32_t n_tiles, int32_t& head, int32_t& t) {
+    if (a.n_groups > 0) {
+        const int32_t k = b / a.heads;
+        head = b - k * a.heads;
+        int32_t acc = 0;
+        t = 0;
+        for (int g = 0; g < a.n_groups; ++g) {
+            if (k >= acc && k < acc + a.grp_count[g]) t = a.grp_start[g] + (k - acc);
+            acc += a.grp_count[g];
+        }
+        return;
+    }
+    const int32_t units = n_tiles * a.heads;
     const int32_t x = b % kNumXcd, j = b / kNumXcd;
     const int32_t per = units / kNumXcd, rem = units % kNumXcd;
     const int32_t u = x * per + min(x, rem) + j;  // XCD x runs units [x per + min(x, rem), ...)
@@ -310,7 +329,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char v1[TILEB];
     const int32_t n_tiles = (a.n + BR - 1) / BR;
     int32_t head, qt;
-    unit_of(blockIdx.x, n_tiles * a.heads, n_tiles, head, qt);
+    unit_of(a, blockIdx.x, n_tiles, head, qt);
     const int32_t r0 = qt * BR, r1 = min(r0 + BR, a.n);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -501,7 +520,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dkdv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char vown[BR * ROWB];  // V of the workgroup's keys (B operand of dP)
     const int32_t n_tiles = (a.n + BR - 1) / BR;
     int32_t head, kt;
-    unit_of(blockIdx.x, n_tiles * a.heads, n_tiles, head, kt);
+    unit_of(a, blockIdx.x, n_tiles, head, kt);
     const int32_t c0 = kt * BR;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -734,9 +753,21 @@ hipError_t launch_moba_backward(const MobaBwd& b, hipStream_t s) {
     hipLaunchKernelGGL(bwd_dsum_kernel, dim3((uint32_t)((rows * 16 + 255) / 256)), dim3(256), 0, s, (const __bf16*)b.dout,
                        (const __bf16*)b.out, b.dsum, b.n, b.heads);
     const uint32_t units = (uint32_t)(((b.n + BR - 1) / BR) * b.heads);
+    a.n_groups = b.n_groups_k;
+    for (int g = 0; g < kMaxGroups; ++g) {
+        a.grp_start[g] = b.grp_k_start[g];
+        a.grp_count[g] = b.grp_k_count[g];
+    }
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(units), dim3(NT), 0, s, a);
+    a.n_groups = b.n_groups_q;
+    for (int g = 0; g < kMaxGroups; ++g) {
+        a.grp_start[g] = b.grp_q_start[g];
+        a.grp_count[g] = b.grp_q_count[g];
+    }
     hipLaunchKernelGGL(bwd_dq_kernel, dim3(units), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
+
+int moba_bwd_block() { return BR; }
 
 }  // namespace wmk

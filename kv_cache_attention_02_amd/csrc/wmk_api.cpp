@@ -188,24 +188,9 @@ size_t plan_split(wmk::AttnPlan& p, int head_dim, int32_t tiles_per_unit, int32_
     return need;
 }
 
-// Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
-int32_t moba_qtile_cost(const wmk::MaskShape& m, int32_t q_tokens, int32_t qt) {
-    const int32_t bq = wmk::attn_bf16_block_q(wmk::kWavesLong);  // MoBA runs the 8-wave kernel
-    const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, q_tokens);
-    const int32_t L = m.part_len, cl = m.chunk_len;
-    std::vector<std::pair<int32_t, int32_t>> iv;
-    for (int32_t part = r0 / L; part <= (r1 - 1) / L && part < m.parts; ++part) {
-        const int32_t fa = std::max(r0, part * L) - part * L, fb = std::min(r1, (part + 1) * L) - part * L - 1;
-        const int32_t ka = fa / cl, kb = fb / cl;
-        if (part == 0) {
-            iv.push_back({0, std::min((kb + 1) * cl, L)});
-        } else if (part == 1) {
-            if (kb > 0) iv.push_back({0, kb * cl});
-            iv.push_back({L + ka * cl, L + std::min((kb + 1) * cl, L)});
-        } else {
-            iv.push_back({2 * L, 3 * L});
-        }
-    }
+// Number of 64-wide tiles the union of the half-open intervals iv covers
+// (each rounded out to whole tiles; the kernels' merge rule).
+int32_t tiles_of_union(std::vector<std::pair<int32_t, int32_t>> iv) {
     for (auto& x : iv) x = {x.first / kBK, (x.second + kBK - 1) / kBK};
     std::sort(iv.begin(), iv.end());
     int32_t total = 0, cur_b = -1, cur_e = -1;
@@ -223,27 +208,80 @@ int32_t moba_qtile_cost(const wmk::MaskShape& m, int32_t q_tokens, int32_t qt) {
     return total;
 }
 
-// Longest-first launch order for MoBA: runs of consecutive q-tiles with equal
-// cost, sorted by decreasing cost.  Falls back to the natural order when there
-// are more runs than the kernel's table holds.
-void plan_moba_groups(wmk::AttnPlan& p, const wmk::MaskShape& m, int32_t q_tokens) {
+// Key tiles a q-tile of the MoBA sequence visits (same union rule as the kernel).
+int32_t moba_rows_cost(const wmk::MaskShape& m, int32_t q_tokens, int32_t r0, int32_t r1) {
+    r1 = std::min(r1, q_tokens);
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    std::vector<std::pair<int32_t, int32_t>> iv;
+    for (int32_t part = r0 / L; part <= (r1 - 1) / L && part < m.parts; ++part) {
+        const int32_t fa = std::max(r0, part * L) - part * L, fb = std::min(r1, (part + 1) * L) - part * L - 1;
+        const int32_t ka = fa / cl, kb = fb / cl;
+        if (part == 0) {
+            iv.push_back({0, std::min((kb + 1) * cl, L)});
+        } else if (part == 1) {
+            if (kb > 0) iv.push_back({0, kb * cl});
+            iv.push_back({L + ka * cl, L + std::min((kb + 1) * cl, L)});
+        } else {
+            iv.push_back({2 * L, 3 * L});
+        }
+    }
+    return tiles_of_union(iv);
+}
+
+int32_t moba_qtile_cost(const wmk::MaskShape& m, int32_t q_tokens, int32_t qt) {
+    const int32_t bq = wmk::attn_bf16_block_q(wmk::kWavesLong);  // MoBA runs the 8-wave kernel
+    return moba_rows_cost(m, q_tokens, qt * bq, qt * bq + bq);
+}
+
+// Query tiles of 64 rows a block of keys [c0, c1) of the MoBA sequence is
+// attended by (the dK/dV kernel's walk: the same union rule, transposed --
+// clean key of chunk c: clean rows of chunks >= c and noisy rows of chunks > c;
+// noisy key of chunk c: noisy rows of chunk c; block key: block rows).
+int32_t moba_ktile_cost(const wmk::MaskShape& m, int32_t n, int32_t c0, int32_t c1) {
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    c1 = std::min(c1, n);
+    std::vector<std::pair<int32_t, int32_t>> iv;
+    if (c1 <= c0) return 0;
+    const int32_t pa = c0 / L, pb = (c1 - 1) / L;
+    if (pa <= 0 && 0 <= pb) {
+        const int32_t ca = c0 / cl;
+        iv.push_back({ca * cl, L});
+        if (m.parts > 1) iv.push_back({std::min(L + (ca + 1) * cl, 2 * L), 2 * L});
+    }
+    if (pa <= 1 && 1 <= pb) {
+        const int32_t fa = std::max(c0, L) - L, fb = std::min(c1, 2 * L) - L - 1;
+        iv.push_back({L + (fa / cl) * cl, L + std::min((fb / cl + 1) * cl, L)});
+    }
+    if (pa <= 2 && 2 <= pb) iv.push_back({2 * L, 3 * L});
+    return tiles_of_union(iv);
+}
+
+// Longest-first launch order: runs of consecutive tiles with equal cost,
+// sorted by decreasing cost (stable).  Returns the number of runs, or 0 (the
+// natural order) when there are more runs than the kernels' tables hold.
+int32_t plan_groups(const std::vector<int32_t>& cost, int32_t* grp_start, int32_t* grp_count) {
     struct Run { int32_t start, count, cost; };
     std::vector<Run> runs;
-    for (int32_t qt = 0; qt < p.n_qtiles; ++qt) {
-        const int32_t cost = moba_qtile_cost(m, q_tokens, qt);
-        if (!runs.empty() && runs.back().cost == cost && runs.back().start + runs.back().count == qt)
+    for (int32_t t = 0; t < (int32_t)cost.size(); ++t) {
+        if (!runs.empty() && runs.back().cost == cost[t] && runs.back().start + runs.back().count == t)
             runs.back().count++;
         else
-            runs.push_back({qt, 1, cost});
+            runs.push_back({t, 1, cost[t]});
     }
-    p.n_groups = 0;
-    if ((int)runs.size() > wmk::kMaxGroups) return;
+    if ((int)runs.size() > wmk::kMaxGroups) return 0;
     std::stable_sort(runs.begin(), runs.end(), [](const Run& a, const Run& b) { return a.cost > b.cost; });
     for (size_t i = 0; i < runs.size(); ++i) {
-        p.grp_start[i] = runs[i].start;
-        p.grp_count[i] = runs[i].count;
+        grp_start[i] = runs[i].start;
+        grp_count[i] = runs[i].count;
     }
-    p.n_groups = (int32_t)runs.size();
+    return (int32_t)runs.size();
+}
+
+// Longest-first launch order of the MoBA forward's q-tiles.
+void plan_moba_groups(wmk::AttnPlan& p, const wmk::MaskShape& m, int32_t q_tokens) {
+    std::vector<int32_t> cost(p.n_qtiles);
+    for (int32_t qt = 0; qt < p.n_qtiles; ++qt) cost[qt] = moba_qtile_cost(m, q_tokens, qt);
+    p.n_groups = plan_groups(cost, p.grp_start, p.grp_count);
 }
 
 // FP8 QK^T buffers carved from the caller's workspace (see qk8_layout).
@@ -735,12 +773,24 @@ wmk_status wmk_moba_attention_backward(const wmk_moba_desc* m, const wmk_head_de
         return fail(WMK_ERR_CAPACITY, "the backward needs %zu bytes of workspace, got %zu", need, workspace_bytes);
     if (!aligned16(workspace)) return fail(WMK_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
+    wmk::MobaBwd b;
+    memset(&b, 0, sizeof b);
+    // longest walk first for both kernels (workgroups of 256 rows or keys, 64-wide tiles)
+    const int32_t n = call.q_tokens, br = wmk::moba_bwd_block(), nt = (n + br - 1) / br;
+    std::vector<int32_t> cost_q(nt), cost_k(nt);
+    for (int32_t t = 0; t < nt; ++t) {
+        cost_q[t] = moba_rows_cost(call.mask, n, t * br, t * br + br);
+        cost_k[t] = moba_ktile_cost(call.mask, n, t * br, t * br + br);
+    }
+    b.n_groups_q = plan_groups(cost_q, b.grp_q_start, b.grp_q_count);
+    b.n_groups_k = plan_groups(cost_k, b.grp_k_start, b.grp_k_count);
     if (dry_run_path() != nullptr) {
-        dry_log("moba_bwd n=%d heads=%d part=%d chunk=%d parts=%d\n", call.q_tokens, call.heads, call.mask.part_len,
-                call.mask.chunk_len, call.mask.parts);
+        dry_log("moba_bwd n=%d heads=%d part=%d chunk=%d parts=%d groups_q=%d groups_k=%d\n", call.q_tokens,
+                call.heads, call.mask.part_len, call.mask.chunk_len, call.mask.parts, b.n_groups_q, b.n_groups_k);
+        for (int g = 0; g < b.n_groups_q; ++g) dry_log("bgroup q %d %d\n", b.grp_q_start[g], b.grp_q_count[g]);
+        for (int g = 0; g < b.n_groups_k; ++g) dry_log("bgroup k %d %d\n", b.grp_k_start[g], b.grp_k_count[g]);
         return ok();
     }
-    wmk::MobaBwd b;
     b.q = q;
     b.k = k;
     b.v = v;

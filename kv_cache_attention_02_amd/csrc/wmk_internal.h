@@ -148,8 +148,17 @@ struct MobaBwd {
     int32_t heads;
     float scale;
     MaskShape mask;
+    // launch order, longest walk first, of the 256-row tiles (dQ kernel) and of
+    // the 256-key tiles (dK/dV kernel): runs of consecutive tiles, all heads of
+    // a tile together (0 groups: the natural order)
+    int32_t n_groups_q, n_groups_k;
+    int32_t grp_q_start[kMaxGroups], grp_q_count[kMaxGroups];
+    int32_t grp_k_start[kMaxGroups], grp_k_count[kMaxGroups];
 };
 hipError_t launch_moba_backward(const MobaBwd& b, hipStream_t s);
+
+// Rows (dQ kernel) or keys (dK/dV kernel) a workgroup of the backward owns.
+int moba_bwd_block();
 
 // Library-held split-tail scratch of wmk_chunk_attention_noalloc: its size,
 // and the device address of the current device's copy (looked up on the

@@ -613,8 +613,58 @@ def test_moba_train_and_backward_argument_errors(lib, dry):
     assert fwd() == wmk.WMK_OK
     assert _last_attn(dry)["mask"] == "1"
     assert bwd() == wmk.WMK_OK
-    last = dry.read_text().strip().splitlines()[-1]
-    assert last == f"moba_bwd n={n} heads=12 part={21 * 1560} chunk={3 * 1560} parts=3"
+    last = [x for x in dry.read_text().strip().splitlines() if x.startswith("moba_bwd")][-1]
+    assert last.startswith(f"moba_bwd n={n} heads=12 part={21 * 1560} chunk={3 * 1560} parts=3 ")
+
+
+def _bwd_order(dry, which):
+    lines = dry.read_text().splitlines()
+    last = max(i for i, x in enumerate(lines) if x.startswith("moba_bwd"))
+    runs = [tuple(int(v) for v in x.split()[2:]) for x in lines[last + 1:] if x.startswith(f"bgroup {which} ")]
+    return [s + i for s, c in runs for i in range(c)]
+
+
+@pytest.mark.parametrize("tpf,frames,cf", [(40, 7, 3), (64, 6, 2), (1560, 21, 3)])
+def test_moba_backward_launch_order_is_longest_first(lib, dry, tpf, frames, cf):
+    """Both backward kernels launch their 256-row (dQ) and 256-key (dK/dV) tiles longest walk first:
+    each order is a permutation of the tiles, and the number of 64-wide tiles each one walks --
+    counted here from the oracle's per-row intervals (rows for dQ; for dK/dV the query tiles
+    holding some row that allows a key of the block) -- never increases along it."""
+    hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
+    md = wmk.wmk_moba_desc(tpf, frames, cf, 1)
+    need = lib.wmk_moba_backward_workspace_bytes(ctypes.byref(md), ctypes.byref(hd))
+    assert lib.wmk_moba_attention_backward(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, SBUF,
+                                           0x70000000, 0x71000000, 0x72000000, 0x73000000, 0.088, 0x60000000, need,
+                                           None) == wmk.WMK_OK
+    n = 3 * frames * tpf
+    nt = (n + 255) // 256
+    oq, ok = _bwd_order(dry, "q"), _bwd_order(dry, "k")
+    assert sorted(oq) == list(range(nt)) and sorted(ok) == list(range(nt))
+    step = 1 if nt < 100 else 5
+    iv = [oracle.moba_row_intervals(i, tpf, frames, cf) for i in range(n)]
+
+    def q_cost(t):
+        tiles = set()
+        for i in range(t * 256, min(t * 256 + 256, n)):
+            for a, b in iv[i]:
+                tiles.update(range(a // 64, (b + 63) // 64))
+        return len(tiles)
+
+    def k_cost(t):
+        # a row tile is walked when some row of it allows a key of [c0, c1): rows of one chunk share
+        # their intervals, so test one row per (64-row tile, chunk boundary) piece
+        c0, c1 = t * 256, min(t * 256 + 256, n)
+        walked = set()
+        for i in range(n):
+            if i // 64 in walked:
+                continue
+            if any(a < c1 and c0 < b for a, b in iv[i]):
+                walked.add(i // 64)
+        return len(walked)
+
+    for order, cost in ((oq, q_cost), (ok, k_cost)):
+        costs = [cost(t) for t in order[::step]]
+        assert all(a >= b for a, b in zip(costs, costs[1:])), costs
 
 
 # ---- the Python binding's own argument checks (raised before any library call)
