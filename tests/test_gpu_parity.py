@@ -140,6 +140,9 @@ def test_append_evict_bit_exact(wmk, S, W, cf, tpf, H, D, n_app, dt):
     dict(S=0, W=2, cf=1, tpf=50, H=2, D=128, warm=0, nq=1, extra=0),      # empty cache, one query
     dict(S=3, W=4, cf=2, tpf=64, H=1, D=128, warm=6, nq=130, extra=3),    # 4 segments (chunk + 3 extra)
     dict(S=1, W=1, cf=1, tpf=129, H=4, D=128, warm=2, nq=257, extra=1),
+    # more than 32 key tiles (2757 keys): the 8-wave kernel shape; the cases above walk at
+    # most 32 tiles and run the 4-wave shape (128-row q-tiles, two workgroups per CU)
+    dict(S=2, W=5, cf=2, tpf=300, H=2, D=128, warm=6, nq=None, extra=1),
 ])
 def test_chunk_attention_small_all_rows(wmk, case):
     import torch
