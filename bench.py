@@ -475,16 +475,20 @@ def other_workloads(wmk, synth, torch, np, fill, dev, stream, reps, which):
     res = {}
 
     def timed(fn):
+        """Mean and min of `reps` calls issued back to back, each between two events on
+        the stream: one call is enqueued ahead, so the host's launch work for the next
+        call overlaps the running one and the events see GPU time only (a wait for the
+        host between calls would add ~20-30 us to each sub-millisecond call)."""
         fn()
         torch.cuda.synchronize()
-        ms = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        fn()
+        evs[0].record(stream)
+        for i in range(reps):
             fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms.append(a.elapsed_time(b))
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
         return float(np.mean(ms)), float(np.min(ms))
 
     if "moba" in which:
