@@ -171,6 +171,53 @@ def test_chunk_attention_small_all_rows(wmk, case):
     cache.close()
 
 
+def _random_case(seed):
+    """A seeded random chunk-attention case: cache geometry, warm-up, query count and extra
+    segments drawn so that calls land on both kernel shapes (up to and beyond 32 key tiles),
+    with ragged query and key tiles, empty and partly filled caches, 64- and 128-dim heads."""
+    r = np.random.default_rng(1000 + seed)
+    D = int(r.choice([64, 128], p=[0.25, 0.75]))
+    S, W, cf = int(r.integers(0, 4)), int(r.integers(1, 6)), int(r.integers(1, 4))
+    tpf = int(r.integers(17, 400))
+    H = int(r.integers(1, 4))
+    warm = int(r.integers(0, 8))
+    nq = int(r.integers(1, 700))
+    extra = [int(r.integers(1, 300)) for _ in range(int(r.integers(0, 4)))]
+    return dict(S=S, W=W, cf=cf, tpf=tpf, H=H, D=D, warm=warm, nq=nq, extra=extra, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_chunk_attention_random_shapes_all_rows(wmk, seed):
+    """Every row of a dozen seeded random calls (see _random_case) against the oracle, with
+    and without the split-tail workspace."""
+    import torch
+    case = _random_case(seed)
+    S, W, cf, tpf, H, D = (case[x] for x in ("S", "W", "cf", "tpf", "H", "D"))
+    cache = wmk.Cache(num_layers=1, num_heads=H, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=cf)
+    cm = oracle.CacheModel(S, W, tpf, H, D)
+    for a in range(case["warm"]):
+        k = host((cf * tpf, H, D), seed=seed, chunk=a, layer=3, kind=synth.KFIN)
+        v = host((cf * tpf, H, D), seed=seed, chunk=a, layer=3, kind=synth.VFIN)
+        cache.append_evict(0, to_dev(k), to_dev(v), cf)
+        cm.append(k, v, cf)
+    nq = case["nq"]
+    q = host((nq, H, D), seed=seed, layer=4, kind=synth.Q)
+    segs = [(host((nq, H, D), seed=seed, layer=4, kind=synth.K), host((nq, H, D), seed=seed, layer=4, kind=synth.V))]
+    for e, n in enumerate(case["extra"]):
+        segs.append((host((n, H, D), seed=seed, chunk=e + 1, layer=5, kind=synth.KLOC),
+                     host((n, H, D), seed=seed, chunk=e + 1, layer=5, kind=synth.VLOC)))
+    keys = oracle.valid_slots(cm.F, S, W) * tpf + sum(k.shape[0] for k, _ in segs)
+    say(f"random case {case}: {keys} keys")
+    ref = oracle.chunk_attention(cm, q, segs, 1.0 / math.sqrt(D))
+    for use_ws in (False, True):
+        out = wmk.chunk_attention(cache, 0, to_dev(q), [(to_dev(k), to_dev(v)) for k, v in segs],
+                                  use_workspace=use_ws)
+        torch.cuda.synchronize()
+        compare(from_dev(out), ref, BF16_MAX_ABS, BF16_REL_L2, f"seed {seed} all rows ws={use_ws}")
+    cache.close()
+
+
 def test_chunk_attention_no_keys_gives_zeros(wmk):
     import torch
     cache = wmk.Cache(num_layers=1, num_heads=2, head_dim=128, tokens_per_frame=8, sink_frames=1, window_frames=1,
