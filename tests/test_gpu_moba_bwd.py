@@ -76,6 +76,37 @@ def test_moba_backward_small_all_elements(wmk, tpf, frames, cf, bidir, H):
     compare_grad(from_dev(gv), rv, "dv")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_moba_train_and_backward_random_shapes(wmk, seed):
+    """Seeded random MoBA sequences (tokens per frame, frame and chunk counts, with and without
+    the bidirectional block): the forward's output and log-sum-exp and every element of dq,
+    dk and dv against the oracle.  The shapes put chunk and part boundaries anywhere inside
+    the 64- and 256-row tiles, and give the backward's longest-first launch order from a
+    few to many runs of equal walk length."""
+    import torch
+    r = np.random.default_rng(2000 + seed)
+    tpf, frames = int(r.integers(5, 91)), int(r.integers(2, 8))
+    cf, bidir, H, D = int(r.integers(1, frames + 1)), int(r.integers(0, 2)), int(r.integers(1, 3)), 128
+    n = (2 + bidir) * frames * tpf
+    q, k, v, do = _inputs(n, H, D, seed=300 + seed)
+    say(f"moba random seed={seed}: tpf={tpf} frames={frames} cf={cf} bidir={bidir} H={H} n={n}")
+    dq_, dk_, dv_, do_ = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    out, lse = wmk.moba_attention_train(dq_, dk_, dv_, tokens_per_frame=tpf, frames=frames, chunk_frames=cf,
+                                        bidir_block=bidir)
+    gq, gk, gv = wmk.moba_attention_backward(dq_, dk_, dv_, out, do_, lse, tokens_per_frame=tpf, frames=frames,
+                                             chunk_frames=cf, bidir_block=bidir)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(D)
+    ref_out = oracle.moba_attention(q, k, v, tpf, frames, cf, bidir, scale)
+    compare_grad(from_dev(out), ref_out, "out")
+    mask = oracle.moba_mask(tpf, frames, cf, bidir)
+    np.testing.assert_allclose(from_dev(lse), oracle.attention_lse(q, k, mask, scale), rtol=0, atol=2e-3)
+    rq, rk, rv = oracle.moba_attention_backward(q, k, v, do, tpf, frames, cf, bidir, scale)
+    compare_grad(from_dev(gq), rq, "dq")
+    compare_grad(from_dev(gk), rk, "dk")
+    compare_grad(from_dev(gv), rv, "dv")
+
+
 def test_moba_backward_mid_size_all_elements(wmk):
     """21 + 21 + 21 frames of 200 tokens in chunks of 3 (12 600 tokens, 2 heads): every
     element of dq, dk and dv against the oracle.  A clean key of chunk 0 is read by the
