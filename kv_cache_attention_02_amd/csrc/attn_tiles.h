@@ -79,14 +79,25 @@ __device__ __forceinline__ TileRanges merge_ranges(int32_t l0, int32_t h0, int32
 
 template <class Call>
 __device__ __forceinline__ TileRanges tile_ranges(const Call& c, int32_t r0, int32_t r1) {
-    int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
-    if (c.mask.mode == kMaskNone) {
-        set_tiles(l0, h0, 0, c.kv_total);
-    } else if (c.mask.mode == kMaskCross) {  // environment prompt + the local prompts of the tile's chunks
+    // The two masks with at most two ranges, the first starting at key 0, skip
+    // the general sort and merge below (scalar work that every wave of the
+    // workgroup repeats at each unit's start).
+    if (c.mask.mode == kMaskNone) {  // every key: one range
+        const int32_t t = (int32_t)(((uint32_t)c.kv_total + BK - 1) / BK);
+        return TileRanges{0, t, 0, 0, 0, 0, 0, 0, t};
+    }
+    if (c.mask.mode == kMaskCross) {  // environment prompt + the local prompts of the tile's chunks
         const int32_t ca = udiv(r0, c.mask.part_div), cb = udiv(r1 - 1, c.mask.part_div);
-        set_tiles(l0, h0, 0, c.mask.env_len);
-        set_tiles(l1, h1, c.mask.env_len + ca * c.mask.chunk_len, c.mask.env_len + (cb + 1) * c.mask.chunk_len);
-    } else {
+        const int32_t a = c.mask.env_len + ca * c.mask.chunk_len, b = c.mask.env_len + (cb + 1) * c.mask.chunk_len;
+        const int32_t e0 = (int32_t)(((uint32_t)c.mask.env_len + BK - 1) / BK);
+        const int32_t b1 = (int32_t)((uint32_t)a / BK), e1 = (int32_t)(((uint32_t)b + BK - 1) / BK);
+        if (b <= a) return TileRanges{0, e0, 0, 0, 0, 0, 0, 0, e0};                      // no local prompt
+        if (e0 == 0) return TileRanges{b1, e1, 0, 0, 0, 0, 0, 0, e1 - b1};               // no environment prompt
+        if (b1 <= e0) return TileRanges{0, e1, 0, 0, 0, 0, 0, 0, e1};                    // one merged range
+        return TileRanges{0, e0, b1, e1, 0, 0, 0, 0, e0 + (e1 - b1)};                     // two ranges
+    }
+    int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
+    {
         const int32_t L = c.mask.part_len, cl = c.mask.chunk_len;
         const FastDiv pd = c.mask.part_div, cd = c.mask.chunk_div;
         const int32_t pa = udiv(r0, pd), pb = min(udiv(r1 - 1, pd), c.mask.parts - 1);
