@@ -27,7 +27,17 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "attn_bf16_832x464_hbm_counters.txt")
-ATTN_SOURCE = os.path.join(ROOT, "kv_cache_attention_02_amd", "csrc", "attn_bf16.hip")
+# the attention kernel's sources: a change to any of them voids the committed counter figures
+ATTN_SOURCES = [os.path.join(ROOT, "kv_cache_attention_02_amd", "csrc", f)
+                for f in ("attn_bf16.hip", "attn_tiles.h", "fastdiv.h", "wmk_internal.h")]
+
+
+def kernel_sources_hash():
+    """sha256[:16] of the attention kernel's source files, concatenated in ATTN_SOURCES order."""
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 S, W, CF, TPF, H, D = 6, 8, 4, 1508, 12, 128
 
@@ -78,7 +88,7 @@ def pmc_traffic():
     taken on the current kernel source (else None)."""
     if not os.path.exists(PMC_SUMMARY):
         return None
-    src_hash = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+    src_hash = kernel_sources_hash()
     vals = {}
     for line in open(PMC_SUMMARY):
         if ":" in line:
