@@ -84,6 +84,28 @@ def test_cross_train_chunks_ignore_other_prompts(wmk):
             np.testing.assert_array_equal(base[rows], alt[rows])
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_cross_train_random_shapes_all_rows(wmk, seed):
+    """Every row of seeded random multi-chunk sequences against the oracle: chunk lengths,
+    chunk count, environment and local prompt lengths (either may be empty, not both),
+    heads and head_dim drawn at random, with and without the split-tail workspace."""
+    import torch
+    rng = np.random.default_rng(900 + seed)
+    cq, nc = int(rng.integers(1, 1201)), int(rng.integers(1, 7))
+    ne, nl = int(rng.integers(0, 601)), int(rng.integers(0, 401))
+    if ne + nl == 0:
+        nl = 1
+    H, D = int(rng.integers(1, 4)), int(rng.choice([64, 128]))
+    q, k, v = _inputs(cq, nc, ne, nl, H, D, seed=1000 + seed)
+    say(f"cross train random seed {seed}: cq={cq} chunks={nc} env={ne} local={nl} H={H} D={D}")
+    ref = oracle.cross_attention_train(q, k, v, cq, ne, nl, 1 / math.sqrt(D))
+    for use_ws in (False, True):
+        out = wmk.cross_attention_train(to_dev(q), to_dev(k), to_dev(v), chunk_q_tokens=cq, env_tokens=ne,
+                                        local_tokens=nl, use_workspace=use_ws)
+        torch.cuda.synchronize()
+        compare(from_dev(out), ref, BF16_MAX_ABS, BF16_REL_L2, f"seed {seed} all rows ws={use_ws}")
+
+
 def test_cross_train_720p(wmk):
     """720p chunks (4 frames x 3600 tokens, 24 heads) of a 3-chunk sequence with
     512-token environment and local prompts, split tail on: sampled rows."""

@@ -99,6 +99,34 @@ def test_qk8_small_codes_and_all_rows(wmk, S, W, cf, tpf, n_chunks, nseg):
     cache.close()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_qk8_random_shapes_codes_and_all_rows(wmk, seed):
+    """Seeded random FP8 calls: random ring state, frame size, query count and 1-3
+    segments of random length; the quantized codes and scales bit for bit, every row
+    against the quantized oracle."""
+    import torch
+    rng = np.random.default_rng(1100 + seed)
+    S, W, cf = int(rng.integers(0, 5)), int(rng.integers(1, 7)), int(rng.integers(1, 4))
+    tpf, n_chunks, nseg = int(rng.integers(8, 201)), int(rng.integers(0, 10)), int(rng.integers(1, 4))
+    H, D = int(rng.integers(1, 4)), 128
+    cache, cm = _filled(wmk, S, W, cf, tpf, H, D, n_chunks, seed=1200 + seed)
+    nq = int(rng.integers(1, 1001))
+    q = host((nq, H, D), seed=1300 + seed, kind=synth.Q)
+    lens = [int(x) for x in rng.integers(1, 151, size=nseg)]
+    segs = [(host((n, H, D), seed=1400 + 10 * seed + i, kind=synth.K),
+             host((n, H, D), seed=1400 + 10 * seed + i, kind=synth.V)) for i, n in enumerate(lens)]
+    nk = oracle.valid_slots(cm.F, S, W) * tpf + sum(lens)
+    ws = torch.zeros(wmk.qk8_workspace_bytes(H, nq, nk), dtype=torch.uint8, device="cuda")
+    say(f"qk8 random seed {seed}: S={S} W={W} cf={cf} tpf={tpf} chunks={n_chunks} H={H} nq={nq} "
+        f"segments={lens} nk={nk}")
+    out = wmk.chunk_attention_qk8(cache, 0, to_dev(q), [(to_dev(k), to_dev(v)) for k, v in segs], ws=ws)
+    torch.cuda.synchronize()
+    _check_codes(ws, cm, q, segs, H)
+    ref = oracle.chunk_attention_qk8(cm, q, segs, 1 / math.sqrt(D))
+    compare(from_dev(out), ref, BF16_MAX_ABS, BF16_REL_L2, f"seed {seed} all rows")
+    cache.close()
+
+
 def test_qk8_832x464(wmk):
     """Warm 832x464 cache (14 resident frames) + the 6032-token chunk, split tail on:
     codes of every block bit for bit, sampled rows against the quantized oracle and

@@ -124,3 +124,35 @@ def test_retained_832x464_sampled_rows(wmk):
     ref = oracle.chunk_attention(cm, q, [(k, v), (ka, va)], 1 / math.sqrt(D), rows=rows, keep_frames=keep)
     compare(from_dev(out)[rows], ref, BF16_MAX_ABS, BF16_REL_L2, f"{len(rows)} sampled rows")
     cache.close()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_retained_random_shapes_all_rows(wmk, seed):
+    """Every row of seeded random retained calls against the oracle: random cache shape,
+    head_dim 64 or 128, a random subset of the resident frames listed in random order,
+    with or without an auxiliary block, with and without the split-tail workspace."""
+    import torch
+    rng = np.random.default_rng(500 + seed)
+    S, W, cf = int(rng.integers(0, 6)), int(rng.integers(1, 10)), int(rng.integers(1, 5))
+    tpf, H, D = int(rng.integers(20, 201)), int(rng.integers(1, 4)), int(rng.choice([64, 128]))
+    n_chunks = int(rng.integers(2, 10))
+    cache, cm = _filled(wmk, S, W, cf, tpf, H, D, n_chunks, "bf16", seed=600 + seed)
+    res = cm.resident()
+    p = rng.uniform(0.2, 0.9)
+    keep = [int(f) for f in rng.permutation([f for f in res if rng.random() < p])]
+    nq = cf * tpf
+    q, k, v = (host((nq, H, D), seed=700 + seed, kind=t) for t in (synth.Q, synth.K, synth.V))
+    segs = [(k, v)]
+    n_aux = int(rng.integers(0, 151))
+    if n_aux:
+        segs.append((host((n_aux, H, D), seed=800 + seed, kind=synth.KLOC),
+                     host((n_aux, H, D), seed=800 + seed, kind=synth.VLOC)))
+    say(f"retained random seed {seed}: S={S} W={W} cf={cf} tpf={tpf} H={H} D={D} chunks={n_chunks} "
+        f"keep={sorted(keep)} aux={n_aux}")
+    ref = oracle.chunk_attention(cm, q, segs, 1 / math.sqrt(D), keep_frames=keep)
+    for use_ws in (False, True):
+        out = wmk.chunk_attention(cache, 0, to_dev(q), [(to_dev(a), to_dev(b)) for a, b in segs],
+                                  keep_frames=keep, use_workspace=use_ws)
+        torch.cuda.synchronize()
+        compare(from_dev(out), ref, BF16_MAX_ABS, BF16_REL_L2, f"seed {seed} all rows ws={use_ws}")
+    cache.close()
