@@ -130,6 +130,43 @@ def test_append_evict_bit_exact(wmk, S, W, cf, tpf, H, D, n_app, dt):
     cache.close()
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_append_evict_random_sequences_bit_exact(wmk, seed):
+    """Seeded random append sequences over a multi-layer cache: random geometry and dtype,
+    each append to a random layer with a random frame count (from one frame to more than
+    the whole cache holds); after every append the slot maps and the resident slots of
+    every layer equal the oracle's bit for bit (layers not appended to stay unchanged)."""
+    import torch
+    rng = np.random.default_rng(1500 + seed)
+    S, W, cf = int(rng.integers(0, 7)), int(rng.integers(1, 11)), int(rng.integers(1, 6))
+    tpf, H, D = int(rng.integers(1, 201)), int(rng.integers(1, 5)), int(rng.choice([64, 128]))
+    dt = "bf16" if rng.random() < 0.7 else "f32"
+    L = int(rng.integers(1, 4))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    cache = wmk.Cache(num_layers=L, num_heads=H, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=cf, dtype=tdt)
+    cms = [oracle.CacheModel(S, W, tpf, H, D, dtype=np.uint16 if dt == "bf16" else np.float32) for _ in range(L)]
+    view = np.uint16 if dt == "bf16" else np.uint32
+    for a in range(8):
+        layer, n = int(rng.integers(0, L)), int(rng.integers(1, S + 2 * W + 3))
+        say(f"append random seed {seed}: S={S} W={W} tpf={tpf} H={H} D={D} {dt} L={L} #{a} layer {layer} "
+            f"frames {n}")
+        k = host((n * tpf, H, D), dt, seed=1600 + seed, chunk=a, layer=layer, step=4, kind=synth.KFIN)
+        v = host((n * tpf, H, D), dt, seed=1600 + seed, chunk=a, layer=layer, step=4, kind=synth.VFIN)
+        cache.append_evict(layer, to_dev(k), to_dev(v), n)
+        cms[layer].append(k, v, n)
+        torch.cuda.synchronize()
+        for l, cm in enumerate(cms):
+            slots, F = cache.slots(l)
+            assert slots == cm.slot_map().tolist() and F == cm.F, (l, slots, cm.slot_map().tolist())
+            valid = oracle.valid_slots(cm.F, S, W)
+            if valid:
+                kb, vb = cm.slot_buffers()
+                assert np.array_equal(from_dev(cache.k[l, :valid]).view(view), kb[:valid].view(view))
+                assert np.array_equal(from_dev(cache.v[l, :valid]).view(view), vb[:valid].view(view))
+    cache.close()
+
+
 # ----------------------------------------------------------------------------------------------
 # chunk attention, small shapes: every row
 # ----------------------------------------------------------------------------------------------
