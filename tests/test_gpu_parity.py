@@ -356,6 +356,29 @@ def test_moba_small_all_rows(wmk, tpf, frames, cf, H, D, bidir):
     compare(from_dev(out), ref, BF16_MAX_ABS, BF16_REL_L2, "all rows")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_moba_random_shapes_all_rows(wmk, seed):
+    """Every row of seeded random MoBA forward calls against the oracle: tokens per frame,
+    frame and chunk counts (a partial last chunk included), the bidirectional block on or
+    off, heads, head_dim 64 or 128, bf16 or fp32."""
+    import torch
+    r = np.random.default_rng(2100 + seed)
+    tpf, frames = int(r.integers(3, 151)), int(r.integers(1, 9))
+    cf, bidir, H = int(r.integers(1, frames + 1)), int(r.integers(0, 2)), int(r.integers(1, 4))
+    D, dt = int(r.choice([64, 128])), ("bf16" if r.random() < 0.75 else "f32")
+    n = (2 + bidir) * frames * tpf
+    q, k, v = (host((n, H, D), dt, seed=2200 + seed, kind=t) for t in (synth.Q, synth.K, synth.V))
+    say(f"moba random seed {seed}: tpf={tpf} frames={frames} cf={cf} bidir={bidir} H={H} D={D} {dt} n={n}")
+    out = wmk.moba_attention(to_dev(q), to_dev(k), to_dev(v), tokens_per_frame=tpf, frames=frames, chunk_frames=cf,
+                             bidir_block=bidir)
+    torch.cuda.synchronize()
+    ref = oracle.moba_attention(q, k, v, tpf, frames, cf, bidir, 1 / math.sqrt(D))
+    if dt == "bf16":
+        compare(from_dev(out), ref, BF16_MAX_ABS, BF16_REL_L2, f"seed {seed} all rows")
+    else:
+        compare(from_dev(out), ref, F32_MAX_ABS, F32_REL_L2, f"seed {seed} fp32 all rows")
+
+
 def test_moba_fp32_small(wmk):
     import torch
     tpf, frames, cf, H, D = 6, 4, 2, 2, 64
