@@ -66,9 +66,10 @@ def parse():
     ap.add_argument("--append-only", action="store_true",
                     help="run only the rolling-session append/evict loop (30 layers, distinct sources and slots; "
                          "for counter runs) and print its timing")
-    ap.add_argument("--append-workload", default="rolling", choices=["rolling", "720p"],
-                    help="append timed by --append-only: the 832x464 rolling session (74 MB per append), or the "
-                         "720p step's append (354 MB: 4 distinct finalized chunks in turn)")
+    ap.add_argument("--append-workload", default="rolling", choices=["rolling", "720p", "layers30"],
+                    help="append timed by --append-only: the 832x464 rolling session (74 MB per append), the "
+                         "720p step's append (354 MB: 4 distinct finalized chunks in turn), or the rolling "
+                         "session's 30 appends of one chunk as one multi-layer call (2.2 GB)")
     ap.add_argument("--step-profile", action="store_true",
                     help="run the 832x464 call on the step-profile build of the library (libwmk_stepprof.so: "
                          "per-wave shader cycles of each phase of a 64-key step) and print the per-step budget")
@@ -176,6 +177,36 @@ def appends_720p(wmk, synth, torch, fill, stream, reps=4):
     del cache, fin
     torch.cuda.empty_cache()
     return us, 4 * reps, 2.0 * 2 * nq * heads * D * 2
+
+
+def appends_30_layers_one_call(wmk, synth, torch, fill, stream, reps=4):
+    """The rolling session's appends of one finalized chunk to all 30 layers of the 832x464
+    cache as one wmk_cache_append_evict_layers call (copy_layers_kernel): 30 distinct 37 MB
+    sources (1.1 GB, one [30][6032][12][128] tensor each for K and V) into a 3.9 GB cache,
+    2.2 GB moved per call, far beyond the 256 MB Infinity Cache.  4 warm-up calls, then
+    `reps` back to back between two events.  Returns microseconds per call and the bytes
+    per call."""
+    layers = 30
+    nq = CF * TPF
+    cache = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
+                      window_frames=W, chunk_frames=CF)
+    ks, vs = (torch.empty((layers, nq, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    for l in range(layers):
+        ks[l].copy_(fill((nq, H, D), layer=l, step=4, kind=synth.KFIN))
+        vs[l].copy_(fill((nq, H, D), layer=l, step=4, kind=synth.VFIN))
+    for _ in range(4):  # 16 frames appended: 14 resident, the ring has wrapped
+        cache.append_evict_layers(0, ks, vs, CF)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        cache.append_evict_layers(0, ks, vs, CF)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del cache, ks, vs
+    torch.cuda.empty_cache()
+    return us, 2.0 * 2 * layers * nq * H * D * 2
 
 
 def step_profile(wmk, synth, torch, np, fill, stream, flops, workload="832x464"):
@@ -373,6 +404,11 @@ def main():
             res = {"append_evict_720p_us": round(us, 2), "appends": n, "bytes_per_append": nbytes,
                    "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                    "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        elif args.append_workload == "layers30":
+            us, nbytes = appends_30_layers_one_call(wmk, synth, torch, fill, stream, reps=args.steps)
+            res = {"append_evict_30_layers_one_call_us": round(us, 2), "calls": args.steps,
+                   "bytes_per_call": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                   "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
         else:
             us, n = rolling_appends(wmk, synth, torch, fill, stream, reps=args.steps)
             res = {"append_evict_rolling_us": round(us, 2), "appends": n,
@@ -433,6 +469,7 @@ def main():
     # this one-layer cache (4 pooled sources: a working set that fits in the
     # Infinity Cache) for comparison
     roll_us, roll_n = rolling_appends(wmk, synth, torch, fill, stream)
+    layers_us, layers_bytes = appends_30_layers_one_call(wmk, synth, torch, fill, stream)
     n_app = 50
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record(stream)
@@ -485,6 +522,13 @@ def main():
             "GBps": round(append_bytes / (roll_us * 1e-6) / 1e9, 1),
             "frac_hbm": round(append_bytes / (roll_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "us_one_layer_4_sources_in_cache": round(append_b2b_us, 2),
+            "all_30_layers_one_call": {
+                "kernel": "copy_layers_kernel (wmk_cache_append_evict_layers)",
+                "bytes_per_call": layers_bytes,
+                "us_per_call": round(layers_us, 2),
+                "GBps": round(layers_bytes / (layers_us * 1e-6) / 1e9, 1),
+                "frac_hbm": round(layers_bytes / (layers_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            },
             "us_in_step_avg": round(float(append_ms.mean()) * 1e3, 2),
             "us_in_step_median": round(float(np.median(append_ms)) * 1e3, 2),
         },

@@ -150,6 +150,26 @@ void wmk_cache_destroy(wmk_cache* c);
 wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new, const void* v_new,
                                   int32_t n_frames, hipStream_t stream);
 
+/* wmk_cache_append_evict for n_layers consecutive layers [first_layer,
+ * first_layer + n_layers) in one launch: the finalized chunk that every layer
+ * of the model appends after it is generated (the same passages as
+ * wmk_cache_append_evict: "How the cache keeps the world alive" of the
+ * LingBot-World-Infinity page, and "World in World", second paragraph).  Each
+ * layer's attention over the chunk reads its own K/V as a segment, so the
+ * appends of all layers can wait for the end of the finalizing pass and go as
+ * one call.
+ * k_new and v_new are [n_layers][n_frames * tokens_per_frame][heads][head_dim]
+ * in the cache dtype (layer first_layer + i at block i), device memory owned by
+ * the caller and only read here.  The result equals n_layers calls of
+ * wmk_cache_append_evict, bit for bit.  Every layer of the run must hold the
+ * same frame count (a model keeps its layers in step).
+ * Errors: NULL -> WMK_ERR_NULL; n_layers <= 0 or n_frames <= 0 ->
+ * WMK_ERR_SHAPE; a layer outside [0, num_layers), or layers holding different
+ * frame counts -> WMK_ERR_RANGE; misaligned -> WMK_ERR_ALIGN; launch refused ->
+ * WMK_ERR_HIP.  On any error no counter advances and nothing is enqueued. */
+wmk_status wmk_cache_append_evict_layers(wmk_cache* c, int32_t first_layer, int32_t n_layers, const void* k_new,
+                                         const void* v_new, int32_t n_frames, hipStream_t stream);
+
 /* Host-side view of a layer's slots, the bookkeeping of the sink + window
  * cache ("How the cache keeps the world alive": sinks kept at the front, the
  * window sliding behind them; "World in World", second paragraph: 6 anchor and

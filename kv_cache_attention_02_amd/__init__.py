@@ -55,6 +55,7 @@ _SIGNATURES = {
     "wmk_cache_init": (ctypes.c_int, [ctypes.POINTER(wmk_cache_desc), _P, _P, ctypes.c_size_t, ctypes.POINTER(_P)]),
     "wmk_cache_destroy": (None, [_P]),
     "wmk_cache_append_evict": (ctypes.c_int, [_P, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
+    "wmk_cache_append_evict_layers": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P]),
     "wmk_cache_slots": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64)]),
     "wmk_attention_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(wmk_head_desc), ctypes.c_int32]),
@@ -250,6 +251,31 @@ class Cache:
         _on_device(k_new=k_new)
         _check(load().wmk_cache_append_evict(self._h, layer, _ptr(k_new), _ptr(v_new), n_frames,
                                              _stream_ptr(stream)))
+
+    def append_evict_layers(self, first_layer, k_new, v_new, n_frames=None, stream=None):
+        """Append one finalized chunk to layers [first_layer, first_layer + len(k_new)) in one
+        launch: k_new/v_new are [n_layers][n_frames * tokens_per_frame][H][D]."""
+        torch = _torch()
+        tpf, H, D = self.desc.tokens_per_frame, self.desc.num_heads, self.desc.head_dim
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if not isinstance(t, torch.Tensor) or t.dim() != 4:
+                raise ValueError(f"{name} must be a 4-d tensor [n_layers][n_frames * tokens_per_frame][H][D]")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.dtype != self.dtype or t.device != self.k.device:
+                raise ValueError(f"{name} is {t.dtype} on {t.device}, expected {self.dtype} on {self.k.device}")
+            if tuple(t.shape[2:]) != (H, D) or t.shape != k_new.shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected [*][*][{H}][{D}] like k_new")
+        n_layers, rows = k_new.shape[0], k_new.shape[1]
+        if n_frames is None:
+            if rows % tpf:
+                raise ValueError(f"k_new has {rows} rows per layer, not a whole number of {tpf}-token frames")
+            n_frames = rows // tpf
+        if rows != n_frames * tpf:
+            raise ValueError(f"k_new has {rows} rows per layer, {n_frames} frames need {n_frames * tpf}")
+        _on_device(k_new=k_new)
+        _check(load().wmk_cache_append_evict_layers(self._h, first_layer, n_layers, _ptr(k_new), _ptr(v_new),
+                                                    n_frames, _stream_ptr(stream)))
 
     def slots(self, layer):
         n = self.desc.sink_frames + self.desc.window_frames

@@ -580,23 +580,18 @@ wmk_status wmk_cache_init(const wmk_cache_desc* d, void* k_dev, void* v_dev, siz
 
 void wmk_cache_destroy(wmk_cache* c) { delete c; }
 
-wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new, const void* v_new,
-                                  int32_t n_frames, hipStream_t stream) {
-    if (c == nullptr || k_new == nullptr || v_new == nullptr)
-        return fail(WMK_ERR_NULL, "cache, k_new and v_new must not be NULL");
-    const wmk_cache_desc& d = c->d;
-    if (layer < 0 || layer >= d.num_layers)
-        return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, d.num_layers);
-    if (n_frames <= 0) return fail(WMK_ERR_SHAPE, "n_frames %d <= 0", n_frames);
-    if ((int64_t)n_frames * d.tokens_per_frame > INT32_MAX)
-        return fail(WMK_ERR_SHAPE, "n_frames * tokens_per_frame exceeds 2^31 - 1");
-    if (!aligned16(k_new) || !aligned16(v_new)) return fail(WMK_ERR_ALIGN, "k_new/v_new must be 16-byte aligned");
+namespace {
 
-    // Frames still resident after this call: sinks and the last W non-sink
-    // frames; the others would be overwritten by this same call and are skipped.
-    const int64_t F = c->frames[layer];
+// The copies of one append: the frames still resident after it (sinks and the
+// last W non-sink frames; the others would be overwritten by this same call
+// and are skipped) in runs of adjacent slots, each run one K and one V range
+// from k_new/v_new into `layer`.  At most 3 runs (sinks, window up to the ring
+// end, wrapped window).  Returns the number of ranges, or -1 if they do not
+// fit one launch.
+int append_ranges(const wmk_cache* c, int32_t layer, int64_t F, const void* k_new, const void* v_new,
+                  int32_t n_frames, wmk::CopyRange* r) {
+    const wmk_cache_desc& d = c->d;
     const int64_t keep_from = F + n_frames - d.window_frames;
-    wmk::CopyRange r[wmk::kMaxCopy];
     int nr = 0;
     int64_t run_f = -1, run_slot = -1, run_len = 0;
     bool too_many = false;
@@ -625,21 +620,82 @@ wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new
             run_len = 1;
         }
     }
-    flush();  // at most 3 runs (sinks, window up to the ring end, wrapped window)
-    if (too_many) return fail(WMK_ERR_SHAPE, "append maps to more slot ranges than one launch copies");
+    flush();
+    return too_many ? -1 : nr;
+}
+
+void dry_log_ranges(const wmk_cache* c, const void* k_new, const wmk::CopyRange* r, int nr) {
+    for (int i = 0; i < nr; i += 2)
+        dry_log(" %lld:%lld:%lld", (long long)((const char*)r[i].src - (const char*)k_new),
+                (long long)((char*)r[i].dst - c->k), (long long)r[i].bytes);
+    dry_log("\n");
+}
+
+}  // namespace
+
+wmk_status wmk_cache_append_evict(wmk_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                                  int32_t n_frames, hipStream_t stream) {
+    if (c == nullptr || k_new == nullptr || v_new == nullptr)
+        return fail(WMK_ERR_NULL, "cache, k_new and v_new must not be NULL");
+    const wmk_cache_desc& d = c->d;
+    if (layer < 0 || layer >= d.num_layers)
+        return fail(WMK_ERR_RANGE, "layer %d outside [0, %d)", layer, d.num_layers);
+    if (n_frames <= 0) return fail(WMK_ERR_SHAPE, "n_frames %d <= 0", n_frames);
+    if ((int64_t)n_frames * d.tokens_per_frame > INT32_MAX)
+        return fail(WMK_ERR_SHAPE, "n_frames * tokens_per_frame exceeds 2^31 - 1");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(WMK_ERR_ALIGN, "k_new/v_new must be 16-byte aligned");
+
+    const int64_t F = c->frames[layer];
+    wmk::CopyRange r[wmk::kMaxCopy];
+    const int nr = append_ranges(c, layer, F, k_new, v_new, n_frames, r);
+    if (nr < 0) return fail(WMK_ERR_SHAPE, "append maps to more slot ranges than one launch copies");
     if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
     if (dry_run_path() != nullptr) {
         dry_log("append layer=%d F=%lld n=%d ranges=%d", layer, (long long)F, n_frames, nr / 2);
-        for (int i = 0; i < nr; i += 2)
-            dry_log(" %lld:%lld:%lld", (long long)((const char*)r[i].src - (const char*)k_new),
-                    (long long)((char*)r[i].dst - c->k), (long long)r[i].bytes);
-        dry_log("\n");
+        dry_log_ranges(c, k_new, r, nr);
         c->frames[layer] = F + n_frames;
         return ok();
     }
     const hipError_t e = wmk::launch_copy_ranges(r, nr, stream);
     if (e != hipSuccess) return fail(WMK_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
     c->frames[layer] = F + n_frames;
+    return ok();
+}
+
+wmk_status wmk_cache_append_evict_layers(wmk_cache* c, int32_t first_layer, int32_t n_layers, const void* k_new,
+                                         const void* v_new, int32_t n_frames, hipStream_t stream) {
+    if (c == nullptr || k_new == nullptr || v_new == nullptr)
+        return fail(WMK_ERR_NULL, "cache, k_new and v_new must not be NULL");
+    const wmk_cache_desc& d = c->d;
+    if (n_layers <= 0) return fail(WMK_ERR_SHAPE, "n_layers %d <= 0", n_layers);
+    if (first_layer < 0 || first_layer >= d.num_layers || n_layers > d.num_layers - first_layer)
+        return fail(WMK_ERR_RANGE, "layers [%d, %d) outside [0, %d)", first_layer, first_layer + n_layers,
+                    d.num_layers);
+    if (n_frames <= 0) return fail(WMK_ERR_SHAPE, "n_frames %d <= 0", n_frames);
+    if ((int64_t)n_frames * d.tokens_per_frame > INT32_MAX)
+        return fail(WMK_ERR_SHAPE, "n_frames * tokens_per_frame exceeds 2^31 - 1");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(WMK_ERR_ALIGN, "k_new/v_new must be 16-byte aligned");
+    const int64_t F = c->frames[first_layer];
+    for (int32_t l = first_layer + 1; l < first_layer + n_layers; ++l)
+        if (c->frames[l] != F)
+            return fail(WMK_ERR_RANGE, "layer %d holds %lld frames, layer %d holds %lld: one call appends to layers "
+                        "in step only", l, (long long)c->frames[l], first_layer, (long long)F);
+
+    wmk::CopyRange r[wmk::kMaxCopy];
+    const int nr = append_ranges(c, first_layer, F, k_new, v_new, n_frames, r);
+    if (nr < 0) return fail(WMK_ERR_SHAPE, "append maps to more slot ranges than one launch copies");
+    const int64_t src_stride = (int64_t)n_frames * (int64_t)c->frame_bytes;  // one layer's k_new block
+    if (fault_injected()) return fail(WMK_ERR_HIP, "launch refused (WMK_FAULT_INJECT)");
+    if (dry_run_path() != nullptr) {
+        dry_log("append_layers first=%d layers=%d F=%lld n=%d ranges=%d src_stride=%lld dst_stride=%lld", first_layer,
+                n_layers, (long long)F, n_frames, nr / 2, (long long)src_stride, (long long)c->layer_bytes);
+        dry_log_ranges(c, k_new, r, nr);
+        for (int32_t l = first_layer; l < first_layer + n_layers; ++l) c->frames[l] = F + n_frames;
+        return ok();
+    }
+    const hipError_t e = wmk::launch_copy_layers(r, nr, n_layers, src_stride, (int64_t)c->layer_bytes, stream);
+    if (e != hipSuccess) return fail(WMK_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+    for (int32_t l = first_layer; l < first_layer + n_layers; ++l) c->frames[l] = F + n_frames;
     return ok();
 }
 

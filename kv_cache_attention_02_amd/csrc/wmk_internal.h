@@ -177,5 +177,9 @@ struct CopyRange {
 };
 constexpr int kMaxCopy = 8;
 hipError_t launch_copy_ranges(const CopyRange* r, int n, hipStream_t s);
+// the ranges of one layer's append, repeated for `layers` consecutive layers
+// (sources and destinations advanced by the given byte strides per layer)
+hipError_t launch_copy_layers(const CopyRange* r, int n, int32_t layers, int64_t src_stride_bytes,
+                              int64_t dst_stride_bytes, hipStream_t s);
 
 }  // namespace wmk

@@ -166,6 +166,58 @@ def test_append_plan_matches_oracle_policy(lib, dry, S, W, cf, n_appends):
     lib.wmk_cache_destroy(h)
 
 
+@pytest.mark.parametrize("S,W,cf,n_appends", [(6, 8, 4, 8), (0, 3, 1, 7), (2, 3, 5, 4), (3, 1, 2, 5)])
+def test_append_layers_plan_equals_per_layer_appends(lib, dry, S, W, cf, n_appends):
+    """One multi-layer append plans the same ranges as wmk_cache_append_evict on its first
+    layer, with sources one [n_frames * tpf] block and destinations one layer apart, and
+    leaves every layer of the run with the oracle's slot map; layers outside the run are
+    untouched."""
+    tpf, H, D = 3, 2, 64
+    fb = tpf * H * D * 2
+    d = _desc(L=5, H=H, D=D, tpf=tpf, S=S, W=W, cf=cf)
+    _, h = _init(lib, d)
+    _, h1 = _init(lib, d)
+    cm = oracle.CacheModel(S, W, tpf, H, D)
+    for a in range(n_appends):
+        F = cm.F
+        assert lib.wmk_cache_append_evict(h1, 1, QBUF, SBUF, cf, None) == wmk.WMK_OK
+        single = dry.read_text().strip().splitlines()[-1].split(" ")
+        assert lib.wmk_cache_append_evict_layers(h, 1, 3, QBUF, SBUF, cf, None) == wmk.WMK_OK
+        multi = dry.read_text().strip().splitlines()[-1].split(" ")
+        assert multi[:8] == ["append_layers", "first=1", "layers=3", f"F={F}", f"n={cf}", single[4],
+                             f"src_stride={cf * fb}", f"dst_stride={(S + W) * fb}"]
+        assert multi[8:] == single[5:]
+        cm.append(np.zeros((cf * tpf, H, D), np.uint16), np.zeros((cf * tpf, H, D), np.uint16), cf)
+        for layer in (1, 2, 3):
+            assert _slots(lib, h, layer, S + W) == (cm.slot_map().tolist(), cm.F)
+        for layer in (0, 4):
+            assert _slots(lib, h, layer, S + W) == ([-1] * (S + W), 0)
+    lib.wmk_cache_destroy(h)
+    lib.wmk_cache_destroy(h1)
+
+
+def test_append_layers_argument_errors_leave_state(lib, dry):
+    d = _desc(L=4)
+    _, h = _init(lib, d)
+    assert lib.wmk_cache_append_evict_layers(h, 0, 4, QBUF, SBUF, 4, None) == wmk.WMK_OK
+    assert lib.wmk_cache_append_evict(h, 3, QBUF, SBUF, 4, None) == wmk.WMK_OK   # layer 3 now one chunk ahead
+    before = [_slots(lib, h, layer, 14) for layer in range(4)]
+    cases = [((None, 0, 2, QBUF, SBUF, 4), wmk.WMK_ERR_NULL), ((h, 0, 2, None, SBUF, 4), wmk.WMK_ERR_NULL),
+             ((h, 0, 0, QBUF, SBUF, 4), wmk.WMK_ERR_SHAPE), ((h, 0, 2, QBUF, SBUF, 0), wmk.WMK_ERR_SHAPE),
+             ((h, -1, 2, QBUF, SBUF, 4), wmk.WMK_ERR_RANGE), ((h, 3, 2, QBUF, SBUF, 4), wmk.WMK_ERR_RANGE),
+             ((h, 4, 1, QBUF, SBUF, 4), wmk.WMK_ERR_RANGE), ((h, 2, 2, QBUF, SBUF, 4), wmk.WMK_ERR_RANGE),
+             ((h, 0, 4, QBUF, SBUF, 4), wmk.WMK_ERR_RANGE), ((h, 0, 2, QBUF + 4, SBUF, 4), wmk.WMK_ERR_ALIGN)]
+    n_before = len(dry.read_text().splitlines())
+    for args, status in cases:
+        assert lib.wmk_cache_append_evict_layers(*args, None) == status, args
+        assert lib.wmk_last_error()
+    assert len(dry.read_text().splitlines()) == n_before   # nothing planned or launched
+    assert [_slots(lib, h, layer, 14) for layer in range(4)] == before
+    assert lib.wmk_cache_append_evict_layers(h, 0, 3, QBUF, SBUF, 4, None) == wmk.WMK_OK   # layers in step
+    assert [_slots(lib, h, layer, 14)[1] for layer in range(4)] == [8, 8, 8, 8]
+    lib.wmk_cache_destroy(h)
+
+
 def test_append_longer_than_window_skips_overwritten_frames(lib, dry):
     S, W, tpf, H, D = 2, 3, 1, 1, 64
     d = _desc(H=H, D=D, tpf=tpf, S=S, W=W, cf=9)

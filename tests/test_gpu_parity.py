@@ -167,6 +167,41 @@ def test_append_evict_random_sequences_bit_exact(wmk, seed):
     cache.close()
 
 
+@pytest.mark.parametrize("S,W,cf,tpf,H,D,L,first,n_layers,dt", [
+    (6, 8, 4, 1508, 12, 128, 3, 0, 3, "bf16"),   # the 832x464 geometry, every layer in one call
+    (2, 3, 5, 7, 3, 64, 4, 1, 2, "bf16"),        # chunk longer than the window, a middle run of layers
+    (0, 4, 3, 5, 2, 128, 3, 0, 2, "f32"),        # no sinks, ring wraps mid-chunk
+    (3, 1, 2, 33, 1, 64, 2, 1, 1, "bf16"),       # a run of one layer, window of one frame
+])
+def test_append_evict_layers_bit_exact(wmk, S, W, cf, tpf, H, D, L, first, n_layers, dt):
+    """Multi-layer appends: after every call the slot maps and resident slots of each layer
+    of the run equal the oracle's bit for bit, and the layers outside the run stay empty."""
+    import torch
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    view = np.uint16 if dt == "bf16" else np.uint32
+    cache = wmk.Cache(num_layers=L, num_heads=H, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=cf, dtype=tdt)
+    cms = [oracle.CacheModel(S, W, tpf, H, D, dtype=np.uint16 if dt == "bf16" else np.float32) for _ in range(L)]
+    for a in range(5):
+        say(f"append_layers S={S} W={W} cf={cf} tpf={tpf} H={H} D={D} {dt} layers [{first}, {first + n_layers}) "
+            f"of {L} #{a}")
+        k = host((n_layers, cf * tpf, H, D), dt, seed=1700, chunk=a, step=4, kind=synth.KFIN)
+        v = host((n_layers, cf * tpf, H, D), dt, seed=1700, chunk=a, step=4, kind=synth.VFIN)
+        cache.append_evict_layers(first, to_dev(k), to_dev(v), cf)
+        for i in range(n_layers):
+            cms[first + i].append(k[i], v[i], cf)
+        torch.cuda.synchronize()
+        for l, cm in enumerate(cms):
+            slots, F = cache.slots(l)
+            assert slots == cm.slot_map().tolist() and F == cm.F, (l, slots)
+            valid = oracle.valid_slots(cm.F, S, W)
+            if valid:
+                kb, vb = cm.slot_buffers()
+                assert np.array_equal(from_dev(cache.k[l, :valid]).view(view), kb[:valid].view(view))
+                assert np.array_equal(from_dev(cache.v[l, :valid]).view(view), vb[:valid].view(view))
+    cache.close()
+
+
 # ----------------------------------------------------------------------------------------------
 # chunk attention, small shapes: every row
 # ----------------------------------------------------------------------------------------------
