@@ -191,9 +191,9 @@ def appends_30_layers_one_call(wmk, synth, torch, fill, stream, reps=4):
     cache = wmk.Cache(num_layers=layers, num_heads=H, head_dim=D, tokens_per_frame=TPF, sink_frames=S,
                       window_frames=W, chunk_frames=CF)
     ks, vs = (torch.empty((layers, nq, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2))
-    for l in range(layers):
-        ks[l].copy_(fill((nq, H, D), layer=l, step=4, kind=synth.KFIN))
-        vs[l].copy_(fill((nq, H, D), layer=l, step=4, kind=synth.VFIN))
+    for l in range(layers):  # generated in place (no copy kernels beside the calibration copies)
+        fill(None, out=ks[l], layer=l, step=4, kind=synth.KFIN)
+        fill(None, out=vs[l], layer=l, step=4, kind=synth.VFIN)
     for _ in range(4):  # 16 frames appended: 14 resident, the ring has wrapped
         cache.append_evict_layers(0, ks, vs, CF)
     torch.cuda.synchronize()
@@ -384,8 +384,8 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def fill(shape, **key):
-        t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    def fill(shape, out=None, **key):
+        t = torch.empty(shape, dtype=torch.bfloat16, device=dev) if out is None else out
         synth.gpu_fill(t.data_ptr(), t.numel(), seed=args.seed, stream=sptr, **key)
         return t
 
