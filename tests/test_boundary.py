@@ -120,6 +120,8 @@ def test_refused_launch_does_not_advance_state(lib, monkeypatch):
     _, h = _init(lib, d)
     assert lib.wmk_cache_append_evict(h, 0, QBUF, SBUF, 4, None) == wmk.WMK_ERR_HIP
     assert _slots(lib, h, 0, 14) == ([-1] * 14, 0)
+    assert lib.wmk_cache_append_evict_layers(h, 0, 1, QBUF, SBUF, 4, None) == wmk.WMK_ERR_HIP
+    assert _slots(lib, h, 0, 14) == ([-1] * 14, 0)
     hd = wmk.wmk_head_desc(12, 128, wmk.WMK_BF16)
     seg = (wmk.wmk_kv_segment * 1)(wmk.wmk_kv_segment(QBUF, SBUF, 6032))
     assert lib.wmk_chunk_attention(h, 0, ctypes.byref(hd), QBUF, 6032, seg, 1, OBUF, 0.088, None, 0,
