@@ -93,12 +93,19 @@ _lib = None
 
 
 def load():
-    """Load libwmk.so (raises if it is not built) and return the ctypes handle."""
+    """Load libwmk.so (raises if it is not built) and return the ctypes handle.
+
+    torch is imported first: it brings its own HIP runtime, and libwmk.so must bind to
+    that same runtime (already loaded, it satisfies the library's dependency), so that
+    the device memory and streams torch hands over are valid in the library's calls.
+    Loaded the other way round, the process would hold two runtimes and the library's
+    launches would fail."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
                                "(there is no fallback implementation)")
+        import torch  # noqa: F401  (its HIP runtime before the library's dependency)
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             f = getattr(lib, name)

@@ -133,6 +133,7 @@ def _load_gpu():
         path = os.path.join(_DIR, "libsynth_gpu.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (bind to torch's HIP runtime, which owns the memory and streams passed in)
         lib = ctypes.CDLL(path)
         lib.synth_gpu_fill.restype = ctypes.c_int
         lib.synth_gpu_fill.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import as_f32, from_dev, host, say, to_dev
+from tests.gpu_helpers import LSE_ATOL, as_f32, from_dev, host, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def test_moba_backward_small_all_elements(wmk, tpf, frames, cf, bidir, H):
     scale = 1 / math.sqrt(D)
     mask = oracle.moba_mask(tpf, frames, cf, bidir)
     ref_lse = oracle.attention_lse(q, k, mask, scale)
-    np.testing.assert_allclose(from_dev(lse), ref_lse, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(from_dev(lse), ref_lse, rtol=0, atol=LSE_ATOL)
     rq, rk, rv = oracle.moba_attention_backward(q, k, v, do, tpf, frames, cf, bidir, scale)
     compare_grad(from_dev(gq), rq, "dq")
     compare_grad(from_dev(gk), rk, "dk")
@@ -100,7 +100,7 @@ def test_moba_train_and_backward_random_shapes(wmk, seed):
     ref_out = oracle.moba_attention(q, k, v, tpf, frames, cf, bidir, scale)
     compare_grad(from_dev(out), ref_out, "out")
     mask = oracle.moba_mask(tpf, frames, cf, bidir)
-    np.testing.assert_allclose(from_dev(lse), oracle.attention_lse(q, k, mask, scale), rtol=0, atol=2e-3)
+    np.testing.assert_allclose(from_dev(lse), oracle.attention_lse(q, k, mask, scale), rtol=0, atol=LSE_ATOL)
     rq, rk, rv = oracle.moba_attention_backward(q, k, v, do, tpf, frames, cf, bidir, scale)
     compare_grad(from_dev(gq), rq, "dq")
     compare_grad(from_dev(gk), rk, "dk")
