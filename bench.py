@@ -73,9 +73,11 @@ def parse():
     ap.add_argument("--step-profile", action="store_true",
                     help="run the 832x464 call on the step-profile build of the library (libwmk_stepprof.so: "
                          "per-wave shader cycles of each phase of a 64-key step) and print the per-step budget")
-    ap.add_argument("--profile-workload", default="832x464", choices=["832x464", "720p_cross"],
-                    help="call profiled by --step-profile: the 832x464 step, or the 720p chunk's cross-attention "
-                         "(14400 queries x 24 heads over a 512-token environment and a 512-token local prompt)")
+    ap.add_argument("--profile-workload", default="832x464", choices=["832x464", "720p_cross", "832x464_qk8"],
+                    help="call profiled by --step-profile: the 832x464 step, the 720p chunk's cross-attention "
+                         "(14400 queries x 24 heads over a 512-token environment and a 512-token local prompt), "
+                         "or the 832x464 step with the FP8 QK^T (the whole call's time includes its two "
+                         "quantization passes)")
     ap.add_argument("--skip-rates", action="store_true",
                     help="skip the reference rates (MFMA microbenchmark, device-to-device copy)")
     return ap.parse_args()
@@ -238,12 +240,16 @@ def step_profile(wmk, synth, torch, np, fill, stream, flops, workload="832x464")
         q, k, v = (fill((nq, H, D), chunk=4, kind=t) for t in (synth.Q, synth.K, synth.V))
         segs = [(k, v)]
     out = torch.empty_like(q)
+    if workload == "832x464_qk8":
+        call = lambda: wmk.chunk_attention_qk8(cache, 0, q, segs, out=out)  # noqa: E731
+    else:
+        call = lambda: wmk.chunk_attention(cache, 0, q, segs, out=out)  # noqa: E731
     for _ in range(5):
-        wmk.chunk_attention(cache, 0, q, segs, out=out)
+        call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    wmk.chunk_attention(cache, 0, q, segs, out=out)
+    call()
     e1.record(stream)
     torch.cuda.synchronize()
     lib = wmk.load()
