@@ -202,6 +202,54 @@ def test_append_evict_layers_bit_exact(wmk, S, W, cf, tpf, H, D, L, first, n_lay
     cache.close()
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_append_evict_layers_random_runs_bit_exact(wmk, seed):
+    """Seeded random mixes of multi-layer and single-layer appends on a multi-layer cache:
+    single-layer appends put layers out of step; a multi-layer run over layers holding
+    different frame counts is refused (WMK_ERR_RANGE, nothing changes); every accepted
+    call leaves every layer's slot map and slots equal to the oracle's bit for bit."""
+    import torch
+    rng = np.random.default_rng(1800 + seed)
+    S, W, cf = int(rng.integers(0, 5)), int(rng.integers(1, 7)), int(rng.integers(1, 4))
+    tpf, H, D, L = int(rng.integers(1, 120)), int(rng.integers(1, 4)), int(rng.choice([64, 128])), int(rng.integers(2, 6))
+    cache = wmk.Cache(num_layers=L, num_heads=H, head_dim=D, tokens_per_frame=tpf, sink_frames=S, window_frames=W,
+                      chunk_frames=cf)
+    cms = [oracle.CacheModel(S, W, tpf, H, D) for _ in range(L)]
+    refused = 0
+    for a in range(12):
+        first = 0 if rng.random() < 0.4 else int(rng.integers(0, L))
+        n_layers = L - first if rng.random() < 0.5 else int(rng.integers(1, L - first + 1))
+        n = int(rng.integers(1, S + 2 * W + 3))
+        k = host((n_layers, n * tpf, H, D), seed=1900 + seed, chunk=a, step=4, kind=synth.KFIN)
+        v = host((n_layers, n * tpf, H, D), seed=1900 + seed, chunk=a, step=4, kind=synth.VFIN)
+        in_step = len({cms[first + i].F for i in range(n_layers)}) == 1
+        say(f"append_layers random seed {seed}: S={S} W={W} tpf={tpf} H={H} D={D} L={L} #{a} layers "
+            f"[{first}, {first + n_layers}) frames {n} in step {in_step}")
+        if rng.random() < 0.2:    # a single-layer append instead: puts that layer out of step
+            cache.append_evict(first, to_dev(k[0]), to_dev(v[0]), n)
+            cms[first].append(k[0], v[0], n)
+        elif in_step:
+            cache.append_evict_layers(first, to_dev(k), to_dev(v), n)
+            for i in range(n_layers):
+                cms[first + i].append(k[i], v[i], n)
+        else:
+            with pytest.raises(wmk.WmkError) as e:
+                cache.append_evict_layers(first, to_dev(k), to_dev(v), n)
+            assert e.value.status == wmk.WMK_ERR_RANGE
+            refused += 1
+        torch.cuda.synchronize()
+        for l, cm in enumerate(cms):
+            slots, F = cache.slots(l)
+            assert slots == cm.slot_map().tolist() and F == cm.F, (l, slots)
+            valid = oracle.valid_slots(cm.F, S, W)
+            if valid:
+                kb, vb = cm.slot_buffers()
+                assert np.array_equal(from_dev(cache.k[l, :valid]).view(np.uint16), kb[:valid].view(np.uint16))
+                assert np.array_equal(from_dev(cache.v[l, :valid]).view(np.uint16), vb[:valid].view(np.uint16))
+    say(f"refused runs: {refused}")
+    cache.close()
+
+
 # ----------------------------------------------------------------------------------------------
 # chunk attention, small shapes: every row
 # ----------------------------------------------------------------------------------------------
