@@ -10,6 +10,7 @@ import os
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import oracle
 import synth
@@ -188,6 +189,32 @@ def test_resident_frames_fill_slot_prefix(S, W, cf):
     for F in range(0, 60):
         slots = sorted(oracle.slot_of_frame(f, S, W) for f in oracle.resident_frames(F, S, W))
         assert slots == list(range(oracle.valid_slots(F, S, W)))
+
+
+@settings(max_examples=300, deadline=None)
+@given(S=st.integers(0, 6), W=st.integers(1, 8), lens=st.lists(st.integers(1, 20), min_size=1, max_size=12))
+def test_cache_model_matches_the_loop_for_any_append_lengths(S, W, lens):
+    """I4/I5 for appends of any lengths: after each append the cache model holds exactly the
+    frames the frame-level loop keeps (append, then drop the oldest non-anchor frames beyond
+    W), each in its own slot of the prefix, with its own K and V."""
+    cm = oracle.CacheModel(S, W, 1, 1, 1, dtype=np.float32)
+    state, anchors, f = [], [], 0
+    for n in lens:
+        ids = np.arange(f, f + n, dtype=np.float32).reshape(n, 1, 1)
+        cm.append(ids, -ids - 1, n)
+        for _ in range(n):
+            state.append(f)
+            if len(anchors) < S:
+                anchors.append(f)
+            f += 1
+        while len([x for x in state if x not in anchors]) > W:
+            state.remove(min(x for x in state if x not in anchors))
+        assert cm.resident() == sorted(state)
+        assert sorted(oracle.slot_of_frame(x, S, W) for x in state) == list(range(len(state)))
+        kb, vb = cm.slot_buffers()
+        for x in state:
+            slot = oracle.slot_of_frame(x, S, W)
+            assert kb[slot, 0, 0, 0] == x and vb[slot, 0, 0, 0] == -x - 1
 
 
 def test_long_append_keeps_last_window_frames():
