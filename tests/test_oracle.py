@@ -481,6 +481,18 @@ def moba_pair_allowed(i, j, tpf, frames, cf):
     return False
 
 
+@settings(max_examples=150, deadline=None)
+@given(tpf=st.integers(1, 5), frames=st.integers(1, 9), bidir=st.integers(0, 1), data=st.data())
+def test_moba_intervals_match_pairwise_mask_any_shape(tpf, frames, bidir, data):
+    """The row intervals equal M1-M4 stated pairwise for any frame size, frame and chunk
+    count (a partial last chunk included), with and without the bidirectional block."""
+    cf = data.draw(st.integers(1, frames))
+    n = (2 + bidir) * frames * tpf
+    want = np.array([[moba_pair_allowed(i, j, tpf, frames, cf) for j in range(n)] for i in range(n)])
+    ivs = [oracle.moba_row_intervals(i, tpf, frames, cf, bidir) for i in range(n)]
+    np.testing.assert_array_equal(mask_from_intervals(ivs, n), want)
+
+
 @pytest.mark.parametrize("tpf,frames,cf", [(4, 6, 2), (3, 7, 3), (2, 5, 1), (5, 4, 4), (1, 9, 2)])
 def test_moba_intervals_match_pairwise_mask(tpf, frames, cf):
     n = 3 * frames * tpf
@@ -581,6 +593,18 @@ def test_cross_attention_ignores_other_chunks_prompts():
     m[:, ne + 2 * nl: ne + 3 * nl] = True
     ref, _ = dense_masked_softmax(q, allk, allv, m, 0.25)
     np.testing.assert_allclose(a, ref, atol=1e-12)
+
+
+@settings(max_examples=150, deadline=None)
+@given(cq=st.integers(1, 6), nc=st.integers(1, 6), ne=st.integers(0, 7), nl=st.integers(0, 7))
+def test_cross_train_intervals_match_pairwise_rule(cq, nc, ne, nl):
+    """X1 stated pairwise: row i (chunk c = i // cq) reads key j iff j is in the environment
+    prompt or in chunk c's own local prompt; the generator's row intervals say the same."""
+    n_k = ne + nc * nl
+    want = np.array([[j < ne or ne + (i // cq) * nl <= j < ne + (i // cq + 1) * nl for j in range(n_k)]
+                     for i in range(cq * nc)]).reshape(cq * nc, n_k)
+    ivs = [oracle.cross_train_row_intervals(i, cq, ne, nl) for i in range(cq * nc)]
+    np.testing.assert_array_equal(mask_from_intervals(ivs, n_k), want)
 
 
 def _xtrain_case(seed, cq=3, nc=4, ne=2, nl=3, H=2, D=16):
