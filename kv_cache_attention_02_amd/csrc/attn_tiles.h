@@ -1,6 +1,7 @@
 // Key-tile planning shared by the attention kernels: per-row allowed key
 // intervals of the three mask modes, and the union of a block of rows' ranges
-// in 64-key tiles.  Device code only.
+// in 64-key tiles.  Compiled for the device, where the kernels call it, and for
+// the host, where the dry-run planner logs every q-tile's ranges for checking.
 #pragma once
 
 #include "wmk_internal.h"
@@ -23,13 +24,13 @@ struct TileRanges {
 constexpr int32_t kNone = 0x7fffffff;  // empty slot
 
 // Key (or row) indices here are never negative: divide them as unsigned.
-__device__ __forceinline__ int32_t udiv(int32_t n, FastDiv d) { return (int32_t)fastdiv((uint32_t)n, d); }
+__host__ __device__ __forceinline__ int32_t udiv(int32_t n, FastDiv d) { return (int32_t)fastdiv((uint32_t)n, d); }
 
-__device__ __forceinline__ void set_tiles(int32_t& l, int32_t& h, int32_t a, int32_t b) {
+__host__ __device__ __forceinline__ void set_tiles(int32_t& l, int32_t& h, int32_t a, int32_t b) {
     if (b > a) { l = (int32_t)((uint32_t)a / BK); h = (int32_t)(((uint32_t)b + BK - 1) / BK); }
 }
 
-__device__ __forceinline__ void order(int32_t& al, int32_t& ah, int32_t& bl, int32_t& bh) {
+__host__ __device__ __forceinline__ void order(int32_t& al, int32_t& ah, int32_t& bl, int32_t& bh) {
     const bool sw = bl < al;
     const int32_t tl = sw ? bl : al, th = sw ? bh : ah;
     bl = sw ? al : bl;
@@ -38,7 +39,7 @@ __device__ __forceinline__ void order(int32_t& al, int32_t& ah, int32_t& bl, int
     ah = th;
 }
 
-__device__ __forceinline__ void emit(TileRanges& r, int k, int32_t b, int32_t e) {
+__host__ __device__ __forceinline__ void emit(TileRanges& r, int k, int32_t b, int32_t e) {
     r.b0 = k == 0 ? b : r.b0; r.e0 = k == 0 ? e : r.e0;
     r.b1 = k == 1 ? b : r.b1; r.e1 = k == 1 ? e : r.e1;
     r.b2 = k == 2 ? b : r.b2; r.e2 = k == 2 ? e : r.e2;
@@ -47,7 +48,7 @@ __device__ __forceinline__ void emit(TileRanges& r, int k, int32_t b, int32_t e)
 
 // Sort up to four tile ranges (kNone = empty slot) and merge overlapping or
 // touching ones.
-__device__ __forceinline__ TileRanges merge_ranges(int32_t l0, int32_t h0, int32_t l1, int32_t h1, int32_t l2,
+__host__ __device__ __forceinline__ TileRanges merge_ranges(int32_t l0, int32_t h0, int32_t l1, int32_t h1, int32_t l2,
                                                    int32_t h2, int32_t l3, int32_t h3) {
     order(l0, h0, l1, h1);
     order(l2, h2, l3, h3);
@@ -78,7 +79,7 @@ __device__ __forceinline__ TileRanges merge_ranges(int32_t l0, int32_t h0, int32
 }
 
 template <class Call>
-__device__ __forceinline__ TileRanges tile_ranges(const Call& c, int32_t r0, int32_t r1) {
+__host__ __device__ __forceinline__ TileRanges tile_ranges(const Call& c, int32_t r0, int32_t r1) {
     // The two masks with at most two ranges, the first starting at key 0, skip
     // the general sort and merge below (scalar work that every wave of the
     // workgroup repeats at each unit's start).
@@ -116,20 +117,20 @@ __device__ __forceinline__ TileRanges tile_ranges(const Call& c, int32_t r0, int
     return merge_ranges(l0, h0, l1, h1, l2, h2, l3, h3);
 }
 
-__device__ __forceinline__ int32_t tile_at(const TileRanges& r, int32_t it) {
+__host__ __device__ __forceinline__ int32_t tile_at(const TileRanges& r, int32_t it) {
     const int32_t n0 = r.e0 - r.b0, n1 = n0 + (r.e1 - r.b1), n2 = n1 + (r.e2 - r.b2);
     return it < n0 ? r.b0 + it : it < n1 ? r.b1 + (it - n0) : it < n2 ? r.b2 + (it - n1) : r.b3 + (it - n2);
 }
 
 // End (exclusive, in tiles) of the tile range that visit `it` falls in.
-__device__ __forceinline__ int32_t range_end_at(const TileRanges& r, int32_t it) {
+__host__ __device__ __forceinline__ int32_t range_end_at(const TileRanges& r, int32_t it) {
     const int32_t n0 = r.e0 - r.b0, n1 = n0 + (r.e1 - r.b1), n2 = n1 + (r.e2 - r.b2);
     return it < n0 ? r.e0 : it < n1 ? r.e1 : it < n2 ? r.e2 : r.e3;
 }
 
 // Allowed key ranges of one query row (see wmk.h).
 template <class Call>
-__device__ __forceinline__ void row_ranges(const Call& c, int32_t row, int32_t& lo0, int32_t& hi0, int32_t& lo1,
+__host__ __device__ __forceinline__ void row_ranges(const Call& c, int32_t row, int32_t& lo0, int32_t& hi0, int32_t& lo1,
                                            int32_t& hi1) {
     lo1 = 0; hi1 = 0;
     if (c.mask.mode == kMaskNone || row >= c.q_tokens) { lo0 = 0; hi0 = c.kv_total; return; }
@@ -152,7 +153,7 @@ __device__ __forceinline__ void row_ranges(const Call& c, int32_t row, int32_t& 
 // clang) lowered the in-place select "s = ok ? s : -inf" into divergent
 // blocks that overwrote s with -inf for lanes outside the first interval and
 // never restored it for lanes inside the second one.
-__device__ __forceinline__ uint32_t in_range(int32_t j, int32_t lo, int32_t hi) {
+__host__ __device__ __forceinline__ uint32_t in_range(int32_t j, int32_t lo, int32_t hi) {
     return (uint32_t)(j - lo) < (uint32_t)(hi - lo) ? 1u : 0u;
 }
 

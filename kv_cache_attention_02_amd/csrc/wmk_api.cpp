@@ -15,6 +15,7 @@
 #include <string>
 #include <vector>
 
+#include "attn_tiles.h"
 #include "wmk.h"
 #include "wmk_internal.h"
 
@@ -352,6 +353,13 @@ wmk_status run_attention(const wmk::AttnCall& call, wmk_dtype dtype, void* ws, s
             for (int x = 0; x < call.kv.n; ++x)
                 dry_log("span %d %d %llx %llx\n", x, call.kv.end[x], (unsigned long long)(uintptr_t)call.kv.k[x],
                         (unsigned long long)(uintptr_t)call.kv.v[x]);
+            // the key tiles each q-tile's workgroup walks, from the kernels' own planner
+            for (int32_t qt = 0; qt < p.n_qtiles; ++qt) {
+                const int32_t r0 = qt * bq, r1 = std::min(r0 + bq, call.q_tokens);
+                const wmk::tiles::TileRanges tr = wmk::tiles::tile_ranges(call, r0, r1);
+                dry_log("tiles %d %d %d %d %d %d %d %d %d %d %d\n", r0, r1, tr.b0, tr.e0, tr.b1, tr.e1, tr.b2, tr.e2,
+                        tr.b3, tr.e3, tr.total);
+            }
             return ok();
         }
         if (qk8 != nullptr) {

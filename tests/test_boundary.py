@@ -876,3 +876,67 @@ def test_fast_division_is_exact(tmp_path):
     assert r.returncode == 0, r.stdout
     checked, wrong = map(int, r.stdout.split()[-2:])
     assert wrong == 0 and checked > 100_000_000
+
+
+def _logged_tiles(dry, n_before):
+    """The tile lines the last planned attention call logged: {(r0, r1): set of tiles}, plus bq."""
+    lines = dry.read_text().splitlines()[n_before:]
+    out = {}
+    for ln in lines:
+        if ln.startswith("tiles "):
+            r0, r1, b0, e0, b1, e1, b2, e2, b3, e3, total = (int(x) for x in ln.split()[1:])
+            tiles = set(range(b0, e0)) | set(range(b1, e1)) | set(range(b2, e2)) | set(range(b3, e3))
+            assert total == (e0 - b0) + (e1 - b1) + (e2 - b2) + (e3 - b3) == len(tiles)   # disjoint ranges
+            out[(r0, r1)] = tiles
+    return out
+
+
+def _oracle_tiles(row_intervals, r0, r1):
+    """Tiles of 64 keys that any row in [r0, r1) may read, from the oracle's row intervals."""
+    tiles = set()
+    for i in range(r0, r1):
+        for lo, hi in row_intervals(i):
+            if hi > lo:
+                tiles |= set(range(lo // 64, (hi - 1) // 64 + 1))
+    return tiles
+
+
+def test_planned_key_tiles_equal_the_oracles_row_intervals(lib, dry):
+    """The key tiles every q-tile's workgroup walks (the kernels' own planner, run on the host
+    in dry-run mode) are exactly the 64-key tiles its rows' oracle intervals touch: for seeded
+    random MoBA sequences (with and without the bidirectional block), cross-attention
+    training sequences and plain calls."""
+    rng = np.random.default_rng(77)
+    hd = wmk.wmk_head_desc(2, 128, wmk.WMK_BF16)
+    checked = 0
+    for case in range(40):
+        n_before = len(dry.read_text().splitlines()) if dry.exists() else 0
+        kind = case % 3
+        if kind == 0:
+            tpf, frames = int(rng.integers(1, 200)), int(rng.integers(1, 9))
+            cf, bidir = int(rng.integers(1, frames + 1)), int(rng.integers(0, 2))
+            md = wmk.wmk_moba_desc(tpf, frames, cf, bidir)
+            assert lib.wmk_moba_attention(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.1,
+                                          None) == wmk.WMK_OK
+            n = (2 + bidir) * frames * tpf
+            rows = lambda i: oracle.moba_row_intervals(i, tpf, frames, cf, bidir)  # noqa: E731
+        elif kind == 1:
+            cq, nc = int(rng.integers(1, 700)), int(rng.integers(1, 8))
+            ne, nl = int(rng.integers(0, 600)), int(rng.integers(0, 400))
+            if ne + nl == 0:
+                nl = 1
+            xd = wmk.wmk_xattn_desc(cq, nc, ne, nl)
+            assert lib.wmk_cross_attention_train(ctypes.byref(xd), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, 0.1,
+                                                 None, 0, None) == wmk.WMK_OK
+            n = cq * nc
+            rows = lambda i: oracle.cross_train_row_intervals(i, cq, ne, nl)  # noqa: E731
+        else:
+            n, nk = int(rng.integers(1, 2000)), int(rng.integers(1, 5000))
+            assert _attn(lib, None, 0, hd, n, [(KBUF, VBUF, nk)]) == wmk.WMK_OK
+            rows = lambda i: [(0, nk)]  # noqa: E731
+        logged = _logged_tiles(dry, n_before)
+        assert sum(r1 - r0 for r0, r1 in logged) == n and min(r0 for r0, _ in logged) == 0
+        for (r0, r1), tiles in logged.items():
+            assert tiles == _oracle_tiles(rows, r0, r1), (case, r0, r1)
+            checked += 1
+    assert checked > 100
