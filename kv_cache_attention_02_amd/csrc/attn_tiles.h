@@ -148,6 +148,49 @@ __host__ __device__ __forceinline__ void row_ranges(const Call& c, int32_t row, 
     else { lo0 = 2 * L; hi0 = 3 * L; }
 }
 
+// Column view of the MoBA mask, for the backward: the query rows that attend
+// key j (at most two ranges).  Transpose of row_ranges: clean key of chunk c -> clean rows
+// of chunks >= c and noisy rows of chunks > c; noisy key of chunk c -> noisy
+// rows of chunk c; block key -> block rows.
+__host__ __device__ __forceinline__ void col_ranges(const MaskShape& m, int32_t n, int32_t j, int32_t& lo0,
+                                                    int32_t& hi0, int32_t& lo1, int32_t& hi1) {
+    lo0 = hi0 = lo1 = hi1 = 0;
+    if (j >= n) return;
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    const int32_t part = udiv(j, m.part_div), c = udiv(j - part * L, m.chunk_div);
+    if (part == 0) {
+        lo0 = c * cl; hi0 = L;
+        lo1 = min(L + (c + 1) * cl, 2 * L); hi1 = m.parts > 1 ? 2 * L : lo1;
+    } else if (part == 1) {
+        lo0 = L + c * cl; hi0 = L + min((c + 1) * cl, L);
+    } else {
+        lo0 = 2 * L; hi0 = 3 * L;
+    }
+}
+
+// Union over keys [c0, c1) of their query ranges, in 64-row tiles (same form as
+// tile_ranges for rows).
+__host__ __device__ __forceinline__ TileRanges col_tile_ranges(const MaskShape& m, int32_t n, int32_t c0,
+                                                               int32_t c1) {
+    int32_t l0 = kNone, h0 = kNone, l1 = kNone, h1 = kNone, l2 = kNone, h2 = kNone, l3 = kNone, h3 = kNone;
+    const int32_t L = m.part_len, cl = m.chunk_len;
+    c1 = min(c1, n);
+    if (c1 > c0) {
+        const int32_t pa = udiv(c0, m.part_div), pb = udiv(c1 - 1, m.part_div);
+        if (pa <= 0 && 0 <= pb) {  // clean keys: from the first key's chunk on, clean and (later) noisy rows
+            const int32_t ca = udiv(c0, m.chunk_div);
+            set_tiles(l0, h0, ca * cl, L);
+            if (m.parts > 1) set_tiles(l1, h1, min(L + (ca + 1) * cl, 2 * L), 2 * L);
+        }
+        if (pa <= 1 && 1 <= pb) {  // noisy keys: the noisy rows of their chunks
+            const int32_t fa = max(c0, L) - L, fb = min(c1, 2 * L) - L - 1;
+            set_tiles(l2, h2, L + udiv(fa, m.chunk_div) * cl, L + min((udiv(fb, m.chunk_div) + 1) * cl, L));
+        }
+        if (pa <= 2 && 2 <= pb) set_tiles(l3, h3, 2 * L, 3 * L);
+    }
+    return merge_ranges(l0, h0, l1, h1, l2, h2, l3, h3);
+}
+
 // j in [lo, hi), without branches.  The masks are written branch-free on
 // purpose: with short-circuit && / || per lane, this toolchain (ROCm 7.2
 // clang) lowered the in-place select "s = ok ? s : -inf" into divergent

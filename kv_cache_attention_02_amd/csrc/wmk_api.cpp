@@ -853,6 +853,13 @@ wmk_status wmk_moba_attention_backward(const wmk_moba_desc* m, const wmk_head_de
                 call.heads, call.mask.part_len, call.mask.chunk_len, call.mask.parts, b.n_groups_q, b.n_groups_k);
         for (int g = 0; g < b.n_groups_q; ++g) dry_log("bgroup q %d %d\n", b.grp_q_start[g], b.grp_q_count[g]);
         for (int g = 0; g < b.n_groups_k; ++g) dry_log("bgroup k %d %d\n", b.grp_k_start[g], b.grp_k_count[g]);
+        // the query tiles each key block's dK/dV workgroup walks, from the kernel's own planner
+        const int32_t br = wmk::moba_bwd_block();
+        for (int32_t c0 = 0; c0 < call.q_tokens; c0 += br) {
+            const wmk::tiles::TileRanges tr = wmk::tiles::col_tile_ranges(call.mask, call.q_tokens, c0, c0 + br);
+            dry_log("ktiles %d %d %d %d %d %d %d %d %d %d %d\n", c0, std::min(c0 + br, call.q_tokens), tr.b0, tr.e0,
+                    tr.b1, tr.e1, tr.b2, tr.e2, tr.b3, tr.e3, tr.total);
+        }
         return ok();
     }
     b.q = q;

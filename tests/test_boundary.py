@@ -940,3 +940,37 @@ def test_planned_key_tiles_equal_the_oracles_row_intervals(lib, dry):
             assert tiles == _oracle_tiles(rows, r0, r1), (case, r0, r1)
             checked += 1
     assert checked > 100
+
+
+def test_planned_backward_query_tiles_equal_the_oracles_mask(lib, dry):
+    """The query tiles every 256-key block's dK/dV workgroup walks (the kernel's own column
+    planner, run on the host in dry-run mode) are exactly the 64-row tiles holding some row
+    that the oracle's MoBA mask lets see a key of the block, for seeded random sequences with
+    and without the bidirectional block."""
+    rng = np.random.default_rng(78)
+    hd = wmk.wmk_head_desc(2, 128, wmk.WMK_BF16)
+    checked = 0
+    for case in range(16):
+        tpf, frames = int(rng.integers(1, 120)), int(rng.integers(1, 8))
+        cf, bidir = int(rng.integers(1, frames + 1)), int(rng.integers(0, 2))
+        md = wmk.wmk_moba_desc(tpf, frames, cf, bidir)
+        need = lib.wmk_moba_backward_workspace_bytes(ctypes.byref(md), ctypes.byref(hd))
+        n_before = len(dry.read_text().splitlines()) if dry.exists() else 0
+        assert lib.wmk_moba_attention_backward(ctypes.byref(md), ctypes.byref(hd), QBUF, KBUF, VBUF, OBUF, SBUF,
+                                               0x70000000, 0x71000000, 0x72000000, 0x73000000, 0.088, 0x60000000,
+                                               need, None) == wmk.WMK_OK
+        n = (2 + bidir) * frames * tpf
+        mask = oracle.moba_mask(tpf, frames, cf, bidir)          # [row][key]
+        blocks = 0
+        for ln in dry.read_text().splitlines()[n_before:]:
+            if not ln.startswith("ktiles "):
+                continue
+            c0, c1, b0, e0, b1, e1, b2, e2, b3, e3, total = (int(x) for x in ln.split()[1:])
+            tiles = set(range(b0, e0)) | set(range(b1, e1)) | set(range(b2, e2)) | set(range(b3, e3))
+            assert total == (e0 - b0) + (e1 - b1) + (e2 - b2) + (e3 - b3) == len(tiles)
+            rows = np.flatnonzero(mask[:, c0:c1].any(axis=1))
+            assert tiles == set((rows // 64).tolist()), (case, c0, c1)
+            blocks += 1
+            checked += 1
+        assert blocks == (n + 255) // 256
+    assert checked >= 40
