@@ -26,6 +26,9 @@
  * - Every call that does GPU work only enqueues it on the given stream and
  *   returns.  Calls on one cache must be issued on one stream (or ordered by
  *   the caller); host-side counters advance when the work is enqueued.
+ * - A cache handle is host state without a lock: calls on one cache from
+ *   several host threads must be serialized by the caller.  Calls on
+ *   different caches, and the calls that take no cache, are independent.
  * - On any error nothing is enqueued, no state changes, and a message is
  *   available from wmk_last_error() on the calling thread.
  */
