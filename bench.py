@@ -80,6 +80,9 @@ def parse():
                          "quantization passes)")
     ap.add_argument("--skip-rates", action="store_true",
                     help="skip the reference rates (MFMA microbenchmark, device-to-device copy)")
+    ap.add_argument("--rates-only", action="store_true",
+                    help="run only the reference rates (MFMA stream, device-to-device copy, fp32 atomic adds) "
+                         "and print them")
     return ap.parse_args()
 
 
@@ -402,6 +405,13 @@ def main():
 
     if args.step_profile:
         print(json.dumps(step_profile(wmk, synth, torch, np, fill, stream, flops, args.profile_workload)))
+        return
+
+    if args.rates_only:
+        rates = reference_rates(torch, stream, append_bytes)
+        rates["rates_source_sha256_16"] = hashlib.sha256(
+            open(os.path.join(ROOT, "kv_cache_attention_02_amd", "csrc", "rates.hip"), "rb").read()).hexdigest()[:16]
+        print(json.dumps(rates))
         return
 
     if args.append_only:
