@@ -1063,13 +1063,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_kernel(Params<NS> prm) {
             // log sum exp of the scaled scores: m_ref and the weights are in log2 units
             if (c.lse != nullptr && h == 0)
                 c.lse[(size_t)head * c.q_tokens + row] = l_tot > 0.0f ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+            // Lane (l32, h) holds dims 8 g + 4 h .. + 3 of its row for g = 0..3.  Per pair
+            // of groups (g0, g1) the lanes l32 and l32 + 32 trade four values, so that
+            // each stores 8 adjacent dims (16 bytes): h = 0 dims 8 g0 .. + 7, h = 1
+            // dims 8 g1 .. + 7 -- 32 contiguous bytes of the row per store.
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 v4 = {o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
-                                o[db][4 * g + 3] * inv};
-                    *(bf16x4*)(op + db * 32 + 8 * g + 4 * h) = __builtin_convertvector(v4, bf16x4);
+                for (int gp = 0; gp < 2; ++gp) {
+                    const int g0 = 2 * gp, g1 = 2 * gp + 1;
+                    const f32x4 a0 = {o[db][4 * g0] * inv, o[db][4 * g0 + 1] * inv, o[db][4 * g0 + 2] * inv,
+                                      o[db][4 * g0 + 3] * inv};
+                    const f32x4 a1 = {o[db][4 * g1] * inv, o[db][4 * g1 + 1] * inv, o[db][4 * g1 + 2] * inv,
+                                      o[db][4 * g1 + 3] * inv};
+                    const bf16x4 b0 = __builtin_convertvector(a0, bf16x4), b1 = __builtin_convertvector(a1, bf16x4);
+                    const uint32_t* p0 = (const uint32_t*)&b0;
+                    const uint32_t* p1 = (const uint32_t*)&b1;
+                    const uint32_t k0 = h ? p1[0] : p0[0], k1 = h ? p1[1] : p0[1];  // kept
+                    const uint32_t s0 = h ? p0[0] : p1[0], s1 = h ? p0[1] : p1[1];  // traded
+                    // the swap returns the lane's own word and its partner's; take the other one
+                    const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+                    const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+                    const uint32_t t0 = r0[0] == s0 ? r0[1] : r0[0], t1 = r1[0] == s1 ? r1[1] : r1[0];
+                    const u32x4 w4 = h ? u32x4{t0, t1, k0, k1} : u32x4{k0, k1, t0, t1};
+                    *(u32x4*)(op + db * 32 + 8 * (h ? g1 : g0)) = w4;
                 }
         }
         return;
